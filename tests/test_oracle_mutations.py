@@ -1,0 +1,42 @@
+"""The pins catch plausible mistakes: each test plants one mistake in a copy
+of the oracle's C source (on the CPU), builds it, and checks that the pin
+suite fails against it."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "mxoracle.c")
+
+MUTANTS = {
+    "ties_away_from_zero": ("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
+    "wrong_emax_e2m1": ("{2, 1, 1, 0, 2, 6.0}", "{2, 1, 1, 0, 1, 6.0}"),
+    "no_saturation": ("q = f->maxnorm; /* saturate */", "q = q;"),
+    "nibbles_swapped": ("if (col % 2 == 0)\n                        *b", "if (col % 2 != 0)\n                        *b"),
+    "rotation_transposed": ("x[c + t] * R[t * r + j]", "x[c + t] * R[j * r + t]"),
+    "zero_sign_dropped": ("if (v == 0.0)\n        return code;", "if (v == 0.0)\n        return 0;"),
+    "scale_clamp_off_by_one": ("if (s < -127)\n        s = -127;", "if (s < -126)\n        s = -126;"),
+    "no_subnormal_grid": ("if (e < f->emin)\n        e = f->emin;\n    double ulp", "double ulp"),
+    "bf16_subnormal_exponent": ("ldexp((double)man, -133)", "ldexp((double)man, -134)"),
+    "scale_from_first_element": ("else if (fabs(y[j]) > amax)", "else if (j == 0)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, name
+    mutant = tmp_path / "mxoracle.c"
+    mutant.write_text(text.replace(old, new))
+    (tmp_path / "mxoracle.h").write_text(open(os.path.join(ROOT, "oracle", "mxoracle.h")).read())
+    lib = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-w",
+                           "-o", str(lib), str(mutant), "-lm"])
+    env = dict(os.environ, MXORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"

@@ -1,0 +1,428 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each test checks the oracle against something it does not share code with:
+hand-worked groups, exhaustive enumerations against a brute-force
+nearest-grid search, closed forms, library conversions (numpy casts and bit
+views), numpy matmul for the rotation, and invariants of the method.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from microscaling_quantize_dequantize_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_groups.json")
+
+E2M1, E4M3 = 0, 1
+EMAX = {E2M1: 2, E4M3: 8}
+SIGN_BIT = {E2M1: 0x8, E4M3: 0x80}
+
+
+# ---- independent descriptions of the element grids -----------------------
+
+def textbook_grid(fmt):
+    """Non-negative finite magnitudes by code, from the OCP MX element
+    definitions: E2M1 {0, .5, 1, 1.5, 2, 3, 4, 6}; E4M3 with bias 7,
+    subnormals m*2^-9, largest finite 448 (code 0x7E), 0x7F is NaN."""
+    if fmt == E2M1:
+        return np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
+    vals = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(vals, dtype=np.float64)
+
+
+def brute_force_codes(fmt, x, s):
+    """Nearest grid point to |x| * 2^-s by exhaustive distance comparison;
+    ties go to the even code; beyond the largest magnitude, the largest."""
+    grid = textbook_grid(fmt)
+    v = np.ldexp(np.abs(x), -np.asarray(s))
+    n = len(grid)
+    hi = np.clip(np.searchsorted(grid, v, side="left"), 1, n - 1)
+    lo = hi - 1
+    d_lo = v - grid[lo]
+    d_hi = grid[hi] - v
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(v >= grid[-1], n - 1, pick)
+    sign = np.signbit(x)
+    return (pick + np.where(sign, SIGN_BIT[fmt], 0)).astype(np.uint8)
+
+
+def all_finite_bf16():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    exp = (bits >> 7) & 0xFF
+    return bits[exp != 0xFF]
+
+
+def bf16_to_f64(bits):
+    return W.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def f64_to_bf16_exact(v):
+    """bf16 bits of values known to be exactly representable."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(v, dtype=np.float64), equal_nan=True)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ---- IEEE decode / encode --------------------------------------------------
+
+def test_bf16_value_matches_bit_view(orc):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = bf16_to_f64(bits)
+    got = np.array([orc.bf16_value(int(b)) for b in bits])
+    assert np.array_equal(got, ref, equal_nan=True)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
+def test_f32_value_matches_bit_view(orc):
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 1 << 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    bits[:4] = [0, 0x80000000, 1, 0x007FFFFF]
+    ref = bits.view(np.float32).astype(np.float64)
+    got = np.array([orc.f32_value(int(b)) for b in bits])
+    assert np.array_equal(got, ref, equal_nan=True)
+
+
+def test_f32_from_double_matches_numpy_cast(orc):
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-160, 130, size=20000))
+    # exact float32 halfway points between neighbours
+    a = rng.standard_normal(2000).astype(np.float32)
+    b = np.nextafter(a, np.float32(np.inf))
+    mid = (a.astype(np.float64) + b.astype(np.float64)) / 2
+    x = np.concatenate([x, mid, [0.0, -0.0, 3.5e38, -3.5e38, 1e-46, 7e-46]])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float32).view(np.uint32)
+    got = np.array([orc.f32_from_double(float(v)) for v in x], dtype=np.uint32)
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_from_double_matches_integer_rne(orc):
+    rng = np.random.default_rng(3)
+    f = (rng.standard_normal(20000) * np.exp2(rng.integers(-140, 127, size=20000))).astype(np.float32)
+    ref = W.f32_to_bf16_bits(f)
+    got = np.array([orc.bf16_from_double(float(v)) for v in f.astype(np.float64)], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_from_double_halfway_and_overflow(orc):
+    bits = all_finite_bf16()
+    bits = bits[(bits & 0x7FFF) < 0x7F7F]  # has a finite upper neighbour
+    lo = bf16_to_f64(bits)
+    hi = bf16_to_f64(bits + 1)
+    mid = (lo + hi) / 2  # exact in double
+    got = np.array([orc.bf16_from_double(float(v)) for v in mid], dtype=np.uint16)
+    even = np.where(bits % 2 == 0, bits, bits + 1).astype(np.uint16)
+    assert np.array_equal(got, even)
+    bmax = orc.bf16_value(0x7F7F)
+    half_ulp = math.ldexp(1.0, 127 - 8)
+    assert orc.bf16_from_double(bmax + half_ulp) == 0x7F80
+    assert orc.bf16_from_double(bmax + half_ulp * 0.99) == 0x7F7F
+    assert orc.bf16_from_double(math.ldexp(1.0, -134)) == 0x0000  # tie -> even (0)
+    assert orc.bf16_from_double(math.ldexp(3.0, -135)) == 0x0001
+
+
+# ---- element format tables ------------------------------------------------
+
+def test_decode_tables(orc):
+    for fmt in (E2M1, E4M3):
+        grid = textbook_grid(fmt)
+        for code, v in enumerate(grid):
+            assert orc.decode(fmt, code) == v
+            neg = orc.decode(fmt, code | SIGN_BIT[fmt])
+            assert neg == -v and math.copysign(1.0, neg) == -1.0
+    assert orc.decode(E4M3, 0x7E) == 448.0
+    assert orc.decode(E4M3, 0x08) == 2.0 ** -6
+    assert orc.decode(E4M3, 0x01) == 2.0 ** -9
+    assert math.isnan(orc.decode(E4M3, 0x7F)) and math.isnan(orc.decode(E4M3, 0xFF))
+    assert np.all(np.diff(textbook_grid(E4M3)) > 0)
+
+
+# ---- scale rule -------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_scale_exponent_exhaustive(orc, fmt):
+    bits = all_finite_bf16()
+    bits = bits[bits < 0x8000]  # amax is non-negative
+    amax = bf16_to_f64(bits)
+    got = np.array([orc.scale_exponent(fmt, float(a)) for a in amax])
+    biased = ((bits >> 7) & 0xFF).astype(np.int64)
+    closed = np.clip(biased - 127 - EMAX[fmt], -127, 127)  # exp field 0 clamps
+    assert np.array_equal(got, closed)
+
+
+# ---- element rounding: exhaustive against brute force ----------------------
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_element_rounding_exhaustive(orc, fmt):
+    x = bf16_to_f64(all_finite_bf16())
+    for s in range(-127, 128):
+        got = orc.encode_n(fmt, x, np.int32(s))
+        ref = brute_force_codes(fmt, x, s)
+        bad = np.flatnonzero(got != ref)
+        assert bad.size == 0, (s, x[bad[:5]], got[bad[:5]], ref[bad[:5]])
+
+
+def test_halfway_points(orc):
+    g = json.load(open(GOLDEN))["halfway_points"]
+    for fmt, key in ((E2M1, "e2m1"), (E4M3, "e4m3")):
+        for v, want in g[key]:
+            code = orc.encode(fmt, v, 0)
+            assert orc.decode(fmt, code) == want, (key, v)
+
+
+# ---- hand-worked groups ---------------------------------------------------
+
+def _group(vals, neg_zero=False):
+    x = np.full((1, 32), -0.0 if neg_zero else 0.0)
+    x[0, :len(vals)] = vals
+    return f64_to_bf16_exact(x)
+
+
+@pytest.mark.parametrize("name", ["W1", "W2", "W3", "W4"])
+def test_hand_worked_group(orc, name):
+    grp = {g["name"]: g for g in json.load(open(GOLDEN))["groups"]}[name]
+    fmt = E2M1 if grp["fmt"] == "e2m1" else E4M3
+    src = _group(grp["input"])
+    codes, scales = orc.quantize(fmt, src)
+    assert scales[0, 0] == grp["scale_byte"]
+    n = len(grp["codes"])
+    if fmt == E2M1:
+        lo, hi = codes[0] & 0xF, codes[0] >> 4
+        unpacked = np.stack([lo, hi], axis=1).ravel()
+        assert list(unpacked[:n]) == grp["codes"]
+        assert list(codes[0, :len(grp["packed_prefix"])]) == grp["packed_prefix"]
+        assert np.all(codes[0, len(grp["packed_prefix"]):] == 0)
+    else:
+        assert list(codes[0, :n]) == grp["codes"]
+        assert np.all(codes[0, n:] == 0)
+    deq = bf16_to_f64(orc.qdq(fmt, src))[0]
+    want = np.zeros(32)
+    want[:n] = grp["dequant"]
+    assert np.array_equal(deq, want)
+    assert np.array_equal(np.signbit(deq[:n]), np.signbit(want[:n]))
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_zero_groups(orc, fmt):
+    for neg in (False, True):
+        src = _group([], neg_zero=neg)
+        codes, scales = orc.quantize(fmt, src)
+        assert scales[0, 0] == 0
+        if fmt == E2M1:
+            assert np.all(codes == (0x88 if neg else 0))
+        else:
+            assert np.all(codes == (0x80 if neg else 0))
+        deq = bf16_to_f64(orc.qdq(fmt, src))
+        assert np.all(deq == 0) and np.all(np.signbit(deq) == neg)
+
+
+# ---- round trips -------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_every_code_round_trips(orc, fmt):
+    grid = textbook_grid(fmt)
+    emax = EMAX[fmt]
+    rows, want_codes, want_bytes = [], [], []
+    for s in range(-127, 128):
+        if emax + s > 127:
+            continue
+        fixer = math.ldexp(1.0, emax + s)  # puts floor(log2 amax) at emax+s
+        for code in range(len(grid)):
+            for sign in (1.0, -1.0):
+                v = sign * math.ldexp(grid[code], s)
+                f = np.float32(v)
+                if float(f) != v or (f.view(np.uint32) & 0xFFFF) != 0:
+                    continue  # not representable in bf16
+                rows.append([fixer, v] + [0.0] * 30)
+                c = code | (SIGN_BIT[fmt] if sign < 0 else 0)
+                want_codes.append(c)
+                want_bytes.append(s + 127)
+    src = f64_to_bf16_exact(np.array(rows))
+    deq = orc.qdq(fmt, src)
+    assert np.array_equal(deq, src)
+    codes, scales = orc.quantize(fmt, src)
+    assert np.array_equal(scales[:, 0], np.array(want_bytes, dtype=np.uint8))
+    got = (codes[:, 0] >> 4) if fmt == E2M1 else codes[:, 1]
+    assert np.array_equal(got, np.array(want_codes, dtype=np.uint8))
+
+
+# ---- invariants on seeded inputs ------------------------------------------
+
+def _inputs():
+    return {
+        "normal": W.random_bf16((16, 256), seed=11),
+        "c1": W.generate("c1")[:8],
+        "c5a": W.generate("c5a", rows=(0, 64))[:, :1024],
+        "tiny": W.random_bf16((8, 128), seed=12, scale=2.0 ** -125),
+        "huge": W.random_bf16((8, 128), seed=13, scale=2.0 ** 120),
+    }
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_qdq_idempotent(orc, fmt):
+    for name, x in _inputs().items():
+        once = orc.qdq(fmt, x)
+        assert np.array_equal(orc.qdq(fmt, once), once), name
+    xf = W.random_f32((8, 256), seed=14)
+    once = orc.qdq(fmt, xf)
+    assert np.array_equal(orc.qdq(fmt, once).view(np.uint32), once.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_qdq_is_dequantized_quantize(orc, fmt):
+    for name, x in _inputs().items():
+        codes, scales = orc.quantize(fmt, x)
+        deq = orc.dequantize(fmt, codes, scales, x.shape[1])
+        assert np.array_equal(deq, orc.qdq(fmt, x)), name
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_dequant_is_code_times_scale(orc, fmt):
+    grid = textbook_grid(fmt)
+    for name, x in _inputs().items():
+        codes, scales = orc.quantize(fmt, x)
+        M, K = x.shape
+        if fmt == E2M1:
+            c = np.stack([codes & 0xF, codes >> 4], axis=2).reshape(M, K)
+        else:
+            c = codes
+        mag = grid[c & (SIGN_BIT[fmt] - 1)]
+        val = np.where(c & SIGN_BIT[fmt], -mag, mag)
+        want = np.ldexp(val, np.repeat(scales.astype(np.int64) - 127, 32, axis=1))
+        got = bf16_to_f64(orc.qdq(fmt, x))
+        assert np.array_equal(got, want), name
+        assert np.array_equal(np.signbit(got), np.signbit(want)), name
+
+
+def test_qdq_error_is_bounded_by_half_step(orc):
+    """|qdq(x) - x| is at most half a grid step at x's binade, or the
+    saturation gap, for every element."""
+    x = W.random_bf16((32, 512), seed=15)
+    xv = bf16_to_f64(x)
+    for fmt in (E2M1, E4M3):
+        mbits = 1 if fmt == E2M1 else 3
+        emin = 0 if fmt == E2M1 else -6
+        maxn = 6.0 if fmt == E2M1 else 448.0
+        _, scales = orc.quantize(fmt, x)
+        s = np.repeat(scales.astype(np.int64) - 127, 32, axis=1)
+        v = np.abs(np.ldexp(xv, -s))
+        e = np.maximum(np.floor(np.log2(np.where(v > 0, v, 1.0))), emin)
+        half = np.ldexp(0.5, (e - mbits).astype(np.int64))
+        err = np.abs(np.ldexp(bf16_to_f64(orc.qdq(fmt, x)), -s) - np.ldexp(xv, -s))
+        assert np.all((err <= half) | (v > maxn))
+
+
+# ---- rotation -----------------------------------------------------------
+
+@pytest.mark.parametrize("r", [16, 32, 64, 128])
+def test_rotation_matches_numpy_matmul(orc, r):
+    rng = np.random.default_rng(r)
+    x = W.random_bf16((4, 2 * 128), seed=r)
+    R = W.f32_to_bf16_bits(rng.standard_normal((r, r)).astype(np.float32))  # non-symmetric
+    y, beta = orc.rotate(x, R, r)
+    xv, Rv = bf16_to_f64(x), bf16_to_f64(R)
+    ref = (xv.reshape(-1, r) @ Rv).reshape(x.shape)          # y = x . R per chunk
+    absref = (np.abs(xv).reshape(-1, r) @ np.abs(Rv)).reshape(x.shape)
+    assert np.all(np.abs(y - ref) <= 1e-12 * absref)
+    assert np.allclose(beta, 1e-5 * absref, rtol=1e-12, atol=0)
+    wrong = (xv.reshape(-1, r) @ Rv.T).reshape(x.shape)      # R . x would differ
+    assert not np.allclose(y, wrong)
+    xf = W.random_f32((3, 128), seed=r + 1)
+    Rf = rng.standard_normal((r, r)).astype(np.float32)
+    yf, _ = orc.rotate(xf, Rf, r)
+    reff = (xf.astype(np.float64).reshape(-1, r) @ Rf.astype(np.float64)).reshape(xf.shape)
+    assert np.allclose(yf, reff, rtol=1e-12, atol=1e-300)
+
+
+@pytest.mark.parametrize("r", [16, 32, 64, 128])
+def test_identity_rotation_is_unrotated(orc, r):
+    x = W.generate("c5a", rows=(0, 64))[:16, :1024]
+    I = f64_to_bf16_exact(np.eye(r))
+    for fmt in (E2M1, E4M3):
+        assert np.array_equal(orc.qdq(fmt, x, I, r), orc.qdq(fmt, x))
+        c0, s0 = orc.quantize(fmt, x)
+        c1, s1 = orc.quantize(fmt, x, I, r)
+        assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+
+
+@pytest.mark.parametrize("r", [16, 64])
+def test_signed_permutation_rotation(orc, r):
+    rng = np.random.default_rng(100 + r)
+    perm = rng.permutation(r)
+    sign = rng.choice([-1.0, 1.0], size=r)
+    P = np.zeros((r, r))
+    P[np.arange(r), perm] = sign                 # y[perm[t]] = sign[t] * x[t]
+    x = W.random_bf16((8, 256), seed=21)
+    xv = bf16_to_f64(x).reshape(-1, r)
+    xp = np.empty_like(xv)
+    xp[:, perm] = xv * sign
+    xp_bits = f64_to_bf16_exact(xp.reshape(x.shape))
+    for fmt in (E2M1, E4M3):
+        assert np.array_equal(orc.qdq(fmt, x, f64_to_bf16_exact(P), r), orc.qdq(fmt, xp_bits))
+
+
+def test_hadamard_one_hot_and_constant(orc):
+    H16 = W.hadamard_rotation(16)
+    assert np.all(np.abs(bf16_to_f64(H16)) == 0.25)
+    x = np.zeros((1, 32))
+    x[0, 3] = 1.0
+    y, beta = orc.rotate(f64_to_bf16_exact(x), H16, 16)
+    assert np.all(np.abs(y[0, :16]) == 0.25) and np.all(y[0, 16:] == 0)
+    assert np.all(beta[0, :16] == 1e-5 * 0.25)
+    codes, scales = orc.quantize(E2M1, f64_to_bf16_exact(x), H16, 16)
+    assert scales[0, 0] == 127 - 4                 # floor(log2 .25) - 2
+    deq = bf16_to_f64(orc.qdq(E2M1, f64_to_bf16_exact(x), H16, 16))
+    assert np.array_equal(deq[0, :16], y[0, :16])  # +-4 * 2^-4
+    for r in (16, 64):
+        H = W.hadamard_rotation(r)
+        c = 0.375
+        n = max(32, r)
+        y, _ = orc.rotate(f64_to_bf16_exact(np.full((1, n), c)), H, r)
+        want = np.zeros(n)
+        want[::r] = c * math.sqrt(r)
+        assert np.array_equal(y[0], want)
+
+
+def test_sylvester_matrix_closed_form(orc):
+    for r in (16, 32, 64, 128):
+        H = W.sylvester_hadamard(r)
+        i, j = np.meshgrid(np.arange(r), np.arange(r), indexing="ij")
+        pop = np.vectorize(lambda v: bin(v).count("1"))(i & j)
+        assert np.array_equal(H, (-1.0) ** pop)
+        Rb = bf16_to_f64(W.hadamard_rotation(r))
+        assert np.all(Rb == Rb[0, 0] * H)
+        assert Rb[0, 0] == orc.bf16_value(orc.bf16_from_double(r ** -0.5))
+        assert np.allclose(Rb @ Rb.T, np.eye(r), atol=3e-3)
+
+
+# ---- non-finite groups (convention; outside the parity bar) ---------------
+
+def test_nonfinite_group(orc):
+    x = np.ones((1, 64))
+    x[0, 5] = np.inf
+    src = f64_to_bf16_exact(x)
+    src[0, 7] = 0x7FC0  # NaN in the same group
+    for fmt in (E2M1, E4M3):
+        codes, scales = orc.quantize(fmt, src)
+        assert scales[0, 0] == 0xFF and scales[0, 1] == 127 - EMAX[fmt]
+        if fmt == E4M3:
+            assert np.all(codes[0, :32] == 0x7F)
+        else:
+            assert np.all(codes[0, :16] == 0)
+        deq = bf16_to_f64(orc.qdq(fmt, src))
+        assert np.all(np.isnan(deq[0, :32])) and np.all(deq[0, 32:] == 1.0)
+
+
+def test_rejects_bad_arguments(orc):
+    x = W.random_bf16((2, 48), seed=1)
+    with pytest.raises(ValueError):
+        orc.qdq(E2M1, x)                      # K % 32 != 0
+    x = W.random_bf16((2, 64), seed=1)
+    with pytest.raises(ValueError):
+        orc.qdq(E2M1, x, W.hadamard_rotation(128), 128)  # K % r != 0
