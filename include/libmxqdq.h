@@ -1,0 +1,140 @@
+/*
+ * libmxqdq -- microscaling (MX) quantize / dequantize on AMD Instinct MI355X
+ * (gfx950, CDNA4).  C ABI: plain pointers and sizes, no framework types.
+ *
+ * The operation (what each call computes):
+ *   - A row-major [M x K] matrix is split along each row into contiguous
+ *     groups of 32 elements; K must be a multiple of 32 ("use cute-dsl to
+ *     speedup mxfp QDQ", Description: group size 32, K divisible by 32,
+ *     contiguous input).
+ *   - Each group gets one shared power-of-two scale from its abs-max
+ *     ("[Transform] [Quantization] Add QuTLASS support to vLLM", Purpose:
+ *     Abs-Max scheme), stored as an E8M0 byte b meaning 2^(b-127) (same page,
+ *     review of vllm/_custom_ops.py: float8_e8m0fnu scale tensor).  Exponent
+ *     rule (OCP MX v1.0; the pages do not print one): s = floor(log2 amax)
+ *     - emax_elem, emax_elem = 2 for E2M1 and 8 for E4M3, clamped to
+ *     [-127, 127]; an all-zero group gets s = -127 (byte 0).
+ *   - Each element y becomes y * 2^-s rounded to nearest, ties to even, onto
+ *     the FP4 E2M1 (MXFP4) or FP8 E4M3 (MXFP8) grid, saturating at 6 / 448.
+ *     The sign of a result that rounds to zero is kept.
+ *   - Optional rotation before the scale ("Add QuTLASS support to vLLM",
+ *     Online rotations: transform + quantization + scale computation fused,
+ *     matrix loaded at runtime, sizes 16/32/64/128): every r-element chunk x
+ *     of a row (chunks start at column 0) is replaced by y = x . R, i.e.
+ *     y[j] = sum_t x[t] * R[t][j], with R an r x r row-major matrix in the
+ *     source dtype, products exact and accumulation in fp32.  For a symmetric
+ *     matrix such as the normalised Hadamard H * r^-0.5 the side does not
+ *     matter.  QDQ then returns the dequantized rotated values (no inverse).
+ *
+ * Layouts:
+ *   src, dst     [M x K] row-major, contiguous, 16-byte aligned.
+ *   codes        E2M1: [M x K/2] bytes, column 2k in bits 3:0 and column
+ *                2k+1 in bits 7:4; E4M3: [M x K] bytes.  16-byte aligned.
+ *   scales       [M x K/32] bytes, row-major, unpadded (the non-swizzled
+ *                [M, K/32] layout of the MXFP8 quantize on the FlashInfer
+ *                cute-dsl digest page, key source excerpt).  4-byte aligned.
+ *   rot          [r x r] row-major in the source dtype, 16-byte aligned.
+ *
+ * Ownership and execution: every pointer is device memory owned by the
+ * caller.  The library allocates nothing, frees nothing and never
+ * synchronizes; every call validates its arguments on the host, enqueues one
+ * kernel on the calling thread's stream (mx_set_stream) and returns.  Calls
+ * are therefore safe to capture in a HIP graph.  dst == src (an exact alias)
+ * is allowed for mx_qdq; any other overlap between inputs and outputs is
+ * undefined.  Faults inside a kernel surface at the caller's next
+ * synchronization, as for any HIP kernel.
+ *
+ * Errors: 0 on success, a negative MX_E* code otherwise; argument errors are
+ * returned before anything is enqueued.  M == 0 or K == 0 is a successful
+ * no-op.  There is no fallback path: unsupported arguments are errors.
+ *
+ * Non-finite input (outside every accuracy contract): a group holding NaN or
+ * Inf gets scale byte 0xFF, E4M3 codes 0x7F (E2M1 codes 0x0), and
+ * dequantized values NaN.
+ */
+#ifndef LIBMXQDQ_H
+#define LIBMXQDQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MX_API __attribute__((visibility("default")))
+
+/* Element formats. */
+#define MX_FMT_E2M1 0 /* MXFP4 */
+#define MX_FMT_E4M3 1 /* MXFP8 */
+
+/* Source / destination dtypes. */
+#define MX_DTYPE_BF16 0
+#define MX_DTYPE_F32 1
+
+/* Status codes. */
+#define MX_OK 0
+#define MX_EFMT (-1)    /* fmt is not MX_FMT_E2M1 / MX_FMT_E4M3            */
+#define MX_EDTYPE (-2)  /* dtype is not MX_DTYPE_BF16 / MX_DTYPE_F32        */
+#define MX_ESHAPE (-3)  /* M < 0, K < 0, K % 32 != 0, or M*K too large      */
+#define MX_EROT (-4)    /* rot_size not in {0,16,32,64,128}, K % rot_size,
+                           or rot == NULL with rot_size > 0                  */
+#define MX_ENULL (-5)   /* a required pointer is NULL                       */
+#define MX_EALIGN (-6)  /* a pointer breaks the alignment stated above      */
+#define MX_ELAUNCH (-7) /* the kernel launch failed (hipGetLastError)       */
+
+/*
+ * Fused quantize-dequantize ("use cute-dsl to speedup mxfp QDQ",
+ * Description: mxfp4_qdq / mxfp8_qdq).
+ *   fmt        MX_FMT_E2M1 or MX_FMT_E4M3.
+ *   src        [M x K] in src_dtype (MX_DTYPE_BF16 or MX_DTYPE_F32).
+ *   rot        NULL, or the r x r rotation in src_dtype; rot_size = r or 0.
+ *   dst        [M x K] in src_dtype: code_value * 2^s, rounded to
+ *              nearest-even into src_dtype (exact whenever representable).
+ */
+MX_API int mx_qdq(int fmt, const void *src, int src_dtype, int64_t M,
+                  int64_t K, const void *rot, int rot_size, void *dst);
+
+/*
+ * Quantize a bf16 matrix to MX codes and E8M0 scales ("Add QuTLASS support
+ * to vLLM", review of vllm/_custom_ops.py: fusedQuantizeMx returning the
+ * E2M1 codes and E8M0 scales; FlashInfer cute-dsl digest page, key source
+ * excerpt: MXFP8 quantize returning (x_q, x_scales)).
+ *   src        [M x K] bf16.
+ *   rot        NULL, or the r x r bf16 rotation; rot_size = r or 0.
+ *   codes      [M x K/2] (E2M1, packed) or [M x K] (E4M3) bytes.
+ *   scales     [M x K/32] E8M0 bytes.
+ */
+MX_API int mx_quantize(int fmt, const void *src, int64_t M, int64_t K,
+                       const void *rot, int rot_size, uint8_t *codes,
+                       uint8_t *scales);
+
+/*
+ * Dequantize codes + scales (the inverse used by the MXFP4 GEMM test on
+ * "Add QuTLASS support to vLLM", review of the test file: a_dq / b_dq built
+ * by a dequantize helper).  dst[i][k] = code_value * 2^(scale-127) rounded
+ * to nearest-even into dst_dtype; a scale byte of 0xFF or an E4M3 NaN code
+ * gives NaN.
+ */
+MX_API int mx_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
+                         int64_t M, int64_t K, int dst_dtype, void *dst);
+
+/*
+ * The rotation step alone: dst[M x K] (fp32) = per-chunk x . R with fp32
+ * accumulation, exactly as the fused calls compute it before the scale.
+ * Exposed so that the rotation's accuracy can be checked directly.
+ */
+MX_API int mx_rotate(const void *src, int src_dtype, int64_t M, int64_t K,
+                     const void *rot, int rot_size, float *dst);
+
+/* Stream used by the calling thread's subsequent calls (a hipStream_t;
+ * NULL = the default stream).  The setting is thread-local. */
+MX_API void mx_set_stream(void *stream);
+MX_API void *mx_get_stream(void);
+
+/* Static, human-readable text for a status code. */
+MX_API const char *mx_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,150 @@
+"""Thin ctypes binding over libmxqdq.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls and takes torch
+tensors on the GPU: it checks that they are contiguous device tensors of the
+expected dtype and shape, points the library at torch's current stream, and
+passes raw pointers.  All computation happens in the HIP kernels; there is
+no fallback: if the library is missing the import fails.
+
+Tensor conventions: bf16 data is ``torch.bfloat16``; codes and scales are
+``torch.uint8``; the rotation is an r x r tensor in the source dtype.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("LIBMXQDQ", os.path.join(_HERE, "libmxqdq.so"))
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libmxqdq.so not found at {LIB_PATH}; build it with "
+                      "`python -m microscaling_quantize_dequantize_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+E2M1, E4M3 = 0, 1
+BF16, F32 = 0, 1
+_DTYPE = {torch.bfloat16: BF16, torch.float32: F32}
+
+_vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+_lib.mx_qdq.argtypes = [_int, _vp, _int, _i64, _i64, _vp, _int, _vp]
+_lib.mx_quantize.argtypes = [_int, _vp, _i64, _i64, _vp, _int, _vp, _vp]
+_lib.mx_dequantize.argtypes = [_int, _vp, _vp, _i64, _i64, _int, _vp]
+_lib.mx_rotate.argtypes = [_vp, _int, _i64, _i64, _vp, _int, _vp]
+_lib.mx_set_stream.argtypes = [_vp]
+_lib.mx_get_stream.restype = _vp
+_lib.mx_status_string.argtypes = [_int]
+_lib.mx_status_string.restype = ctypes.c_char_p
+for _f in (_lib.mx_qdq, _lib.mx_quantize, _lib.mx_dequantize, _lib.mx_rotate):
+    _f.restype = _int
+
+
+class MXError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"libmxqdq status {status}: {mx_status_string(status)}")
+
+
+def mx_status_string(status: int) -> str:
+    return _lib.mx_status_string(int(status)).decode()
+
+
+def mx_set_stream(stream) -> None:
+    """Point the calling thread's library calls at a torch stream or a raw
+    hipStream_t (int)."""
+    _lib.mx_set_stream(ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream))
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _rot(rot, dtype):
+    if rot is None:
+        return None, 0
+    if rot.dtype != dtype or rot.dim() != 2 or rot.shape[0] != rot.shape[1]:
+        raise ValueError("rotation must be a square matrix in the source dtype")
+    return _dev(rot, "rot"), rot.shape[0]
+
+
+def _mk(src: torch.Tensor) -> tuple[int, int]:
+    if src.dim() != 2:
+        raise ValueError("expected a 2-D [M, K] tensor")
+    return src.shape[0], src.shape[1]
+
+
+def _call(status: int) -> None:
+    if status != 0:
+        raise MXError(status)
+
+
+def _stream() -> None:
+    _lib.mx_set_stream(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+
+def mx_qdq(fmt: int, src: torch.Tensor, rot: torch.Tensor | None = None,
+           dst: torch.Tensor | None = None) -> torch.Tensor:
+    """Fused MX quantize-dequantize of src [M, K] (bf16 or fp32) into dst."""
+    M, K = _mk(src)
+    if src.dtype not in _DTYPE:
+        raise TypeError("src must be bfloat16 or float32")
+    if dst is None:
+        dst = torch.empty_like(src)
+    if dst.dtype != src.dtype or dst.shape != src.shape:
+        raise ValueError("dst must match src in dtype and shape")
+    rp, r = _rot(rot, src.dtype)
+    _stream()
+    _call(_lib.mx_qdq(fmt, _dev(src, "src"), _DTYPE[src.dtype], M, K, rp, r, _dev(dst, "dst")))
+    return dst
+
+
+def mx_quantize(fmt: int, src: torch.Tensor, rot: torch.Tensor | None = None,
+                codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """Quantize bf16 src [M, K] -> (codes uint8 [M, K/2 or K], scales uint8 [M, K/32])."""
+    M, K = _mk(src)
+    if src.dtype != torch.bfloat16:
+        raise TypeError("mx_quantize takes bfloat16 input")
+    if codes is None:
+        codes = torch.empty((M, K // 2 if fmt == E2M1 else K), dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=src.device)
+    rp, r = _rot(rot, src.dtype)
+    _stream()
+    _call(_lib.mx_quantize(fmt, _dev(src, "src"), M, K, rp, r, _dev(codes, "codes"),
+                           _dev(scales, "scales")))
+    return codes, scales
+
+
+def mx_dequantize(fmt: int, codes: torch.Tensor, scales: torch.Tensor, K: int,
+                  dtype: torch.dtype = torch.bfloat16, dst: torch.Tensor | None = None):
+    """Dequantize codes + scales into a [M, K] tensor of `dtype`."""
+    M = scales.shape[0]
+    if dst is None:
+        dst = torch.empty((M, K), dtype=dtype, device=codes.device)
+    _stream()
+    _call(_lib.mx_dequantize(fmt, _dev(codes, "codes"), _dev(scales, "scales"), M, K,
+                             _DTYPE[dst.dtype], _dev(dst, "dst")))
+    return dst
+
+
+def mx_rotate(src: torch.Tensor, rot: torch.Tensor, dst: torch.Tensor | None = None):
+    """The rotation step alone: fp32 [M, K] of per-chunk src . rot."""
+    M, K = _mk(src)
+    if dst is None:
+        dst = torch.empty((M, K), dtype=torch.float32, device=src.device)
+    rp, r = _rot(rot, src.dtype)
+    _stream()
+    _call(_lib.mx_rotate(_dev(src, "src"), _DTYPE[src.dtype], M, K, rp, r, _dev(dst, "dst")))
+    return dst
+
+
+def raw():
+    """The ctypes library handle (for callers passing raw pointers)."""
+    return _lib

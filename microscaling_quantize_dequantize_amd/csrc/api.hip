@@ -1,0 +1,132 @@
+// C ABI of libmxqdq: argument validation and kernel selection.  Everything
+// here runs on the host before the single kernel launch of each call; no
+// call allocates, frees or synchronizes.
+#include <stdint.h>
+
+#include "../../include/libmxqdq.h"
+#include "launch.h"
+
+namespace {
+
+thread_local hipStream_t tl_stream = nullptr;
+
+// Largest accepted element count (2^46); far beyond any device memory, and it
+// keeps every 64-bit index computation in range.
+constexpr int64_t MAX_ELEMS = (int64_t)1 << 46;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_fmt(int fmt) { return (fmt == MX_FMT_E2M1 || fmt == MX_FMT_E4M3) ? MX_OK : MX_EFMT; }
+
+int check_dtype(int dt) { return (dt == MX_DTYPE_BF16 || dt == MX_DTYPE_F32) ? MX_OK : MX_EDTYPE; }
+
+int check_shape(int64_t M, int64_t K) {
+  if (M < 0 || K < 0 || K % 32 != 0) return MX_ESHAPE;
+  if (K > 0 && M > MAX_ELEMS / K) return MX_ESHAPE;
+  return MX_OK;
+}
+
+int check_rot(const void *rot, int r, int64_t K, bool allow_none) {
+  if (r == 0) return allow_none ? MX_OK : MX_EROT;
+  if (r != 16 && r != 32 && r != 64 && r != 128) return MX_EROT;
+  if (K % r != 0) return MX_EROT;
+  if (rot == nullptr) return MX_EROT;
+  return MX_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ELAUNCH; }
+
+}  // namespace
+
+namespace mx {
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+}  // namespace mx
+
+extern "C" {
+
+MX_API int mx_qdq(int fmt, const void *src, int src_dtype, int64_t M, int64_t K, const void *rot,
+                  int rot_size, void *dst) {
+  int st;
+  if ((st = check_fmt(fmt)) || (st = check_dtype(src_dtype)) || (st = check_shape(M, K)) ||
+      (st = check_rot(rot, rot_size, K, true)))
+    return st;
+  if (M == 0 || K == 0) return MX_OK;
+  if (!src || !dst) return MX_ENULL;
+  if (!aligned(src, 16) || !aligned(dst, 16) || (rot_size && !aligned(rot, 16))) return MX_EALIGN;
+  const int64_t n = M * K;
+  if (rot_size == 0)
+    return launched(mx::launch_unrot(fmt, mx::OP_QDQ, src_dtype, src, dst, nullptr, nullptr, n, tl_stream));
+  return launched(mx::launch_rot(fmt, mx::OP_QDQ, src_dtype, src, rot, rot_size, dst, nullptr, nullptr, n,
+                                 tl_stream));
+}
+
+MX_API int mx_quantize(int fmt, const void *src, int64_t M, int64_t K, const void *rot, int rot_size,
+                       uint8_t *codes, uint8_t *scales) {
+  int st;
+  if ((st = check_fmt(fmt)) || (st = check_shape(M, K)) || (st = check_rot(rot, rot_size, K, true)))
+    return st;
+  if (M == 0 || K == 0) return MX_OK;
+  if (!src || !codes || !scales) return MX_ENULL;
+  if (!aligned(src, 16) || !aligned(codes, 16) || !aligned(scales, 4) || (rot_size && !aligned(rot, 16)))
+    return MX_EALIGN;
+  const int64_t n = M * K;
+  if (rot_size == 0)
+    return launched(mx::launch_unrot(fmt, mx::OP_QUANT, MX_DTYPE_BF16, src, nullptr, codes, scales, n,
+                                     tl_stream));
+  return launched(mx::launch_rot(fmt, mx::OP_QUANT, MX_DTYPE_BF16, src, rot, rot_size, nullptr, codes, scales,
+                                 n, tl_stream));
+}
+
+MX_API int mx_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales, int64_t M, int64_t K,
+                         int dst_dtype, void *dst) {
+  int st;
+  if ((st = check_fmt(fmt)) || (st = check_dtype(dst_dtype)) || (st = check_shape(M, K))) return st;
+  if (M == 0 || K == 0) return MX_OK;
+  if (!codes || !scales || !dst) return MX_ENULL;
+  if (!aligned(codes, 16) || !aligned(dst, 16)) return MX_EALIGN;
+  return launched(mx::launch_dequant(fmt, dst_dtype, codes, scales, dst, M * K, tl_stream));
+}
+
+MX_API int mx_rotate(const void *src, int src_dtype, int64_t M, int64_t K, const void *rot, int rot_size,
+                     float *dst) {
+  int st;
+  if ((st = check_dtype(src_dtype)) || (st = check_shape(M, K)) || (st = check_rot(rot, rot_size, K, false)))
+    return st;
+  if (M == 0 || K == 0) return MX_OK;
+  if (!src || !dst) return MX_ENULL;
+  if (!aligned(src, 16) || !aligned(dst, 16) || !aligned(rot, 16)) return MX_EALIGN;
+  return launched(mx::launch_rot(0, mx::OP_ROTATE, src_dtype, src, rot, rot_size, dst, nullptr, nullptr, M * K,
+                                 tl_stream));
+}
+
+MX_API void mx_set_stream(void *stream) { tl_stream = (hipStream_t)stream; }
+
+MX_API void *mx_get_stream(void) { return (void *)tl_stream; }
+
+MX_API const char *mx_status_string(int status) {
+  switch (status) {
+    case MX_OK: return "ok";
+    case MX_EFMT: return "invalid format (expected MX_FMT_E2M1 or MX_FMT_E4M3)";
+    case MX_EDTYPE: return "invalid dtype (expected MX_DTYPE_BF16 or MX_DTYPE_F32)";
+    case MX_ESHAPE: return "invalid shape (M, K >= 0, K a multiple of 32, M*K <= 2^46)";
+    case MX_EROT: return "invalid rotation (size 16/32/64/128 dividing K, non-NULL matrix)";
+    case MX_ENULL: return "a required pointer is NULL";
+    case MX_EALIGN: return "misaligned pointer (16 bytes; scales 4 bytes)";
+    case MX_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

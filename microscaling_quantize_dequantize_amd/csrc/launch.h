@@ -1,0 +1,25 @@
+// Internal launchers (host side).  Arguments are validated by the C ABI in
+// api.hip before any of these is called; n is the element count M*K (> 0,
+// a multiple of 32 and of the rotation block).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+enum Op { OP_QDQ = 0, OP_QUANT = 1, OP_ROTATE = 2 };
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+hipError_t launch_unrot(int fmt, int op, int dtype, const void *src, void *dst, uint8_t *codes,
+                        uint8_t *scales, int64_t n, hipStream_t stream);
+
+hipError_t launch_dequant(int fmt, int dtype, const uint8_t *codes, const uint8_t *scales,
+                          void *dst, int64_t n, hipStream_t stream);
+
+hipError_t launch_rot(int fmt, int op, int dtype, const void *src, const void *rot, int r,
+                      void *dst, uint8_t *codes, uint8_t *scales, int64_t n, hipStream_t stream);
+
+}  // namespace mx

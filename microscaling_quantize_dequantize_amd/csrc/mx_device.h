@@ -1,0 +1,224 @@
+// Device helpers for the MX kernels (gfx950 / CDNA4 only).
+//
+// Scale: a group's E8M0 byte comes straight from the exponent field of its
+// abs-max (OCP MX v1.0 rule s = floor(log2 amax) - emax_elem, clamped to
+// [-127, 127]).
+//
+// Elements: the CDNA4 scaled conversions v_cvt_scalef32_pk_{fp4,fp8}_{bf16,
+// f32} take the scale as an fp32 whose exponent field is the E8M0 byte (so
+// byte 0 means 2^-127) and round to nearest-even.  Characterised on gfx950
+// against the CPU oracle over every finite bf16 value and every scale byte:
+// FP4 matches exactly; FP8 matches exactly once the magnitude is first
+// clamped to 448 * 2^s (the hardware returns NaN instead of saturating).  The
+// up-conversions to bf16 round to nearest-even, subnormals included.
+//
+// Software forms of the same steps (quant_mag, decode_mag) are kept for the
+// fp32 outputs, where every value is exact in fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Element formats: OCP MX v1.0 E2M1 (MXFP4) and E4M3 (MXFP8).
+template <int FMT> struct Fmt;
+template <> struct Fmt<0> {
+  static constexpr int mbits = 1, emin = 0, emax = 2, bias = 1, maxcode = 7;
+  static constexpr unsigned sign_bit = 0x8, nan_code = 0x0;
+  static constexpr float maxnorm = 6.0f;
+};
+template <> struct Fmt<1> {
+  static constexpr int mbits = 3, emin = -6, emax = 8, bias = 7, maxcode = 126;
+  static constexpr unsigned sign_bit = 0x80, nan_code = 0x7F;
+  static constexpr float maxnorm = 448.0f;
+};
+
+constexpr unsigned BF16_NAN = 0x7FC0u;
+constexpr unsigned F32_NAN = 0x7FC00000u;
+
+// E8M0 byte of a group from its abs-max laid out as fp32 bits with the sign
+// cleared (a bf16 abs-max is its bits << 16).  The biased exponent e gives
+// floor(log2 amax) = e - 127 (e = 0: zero or subnormal, which clamps), so
+// byte = clamp(e - 127 - emax, -127, 127) + 127 = max(e - emax, 0).
+// 255 marks a group holding NaN or Inf.
+template <int FMT>
+__device__ __forceinline__ unsigned scale_byte(unsigned amax_bits) {
+  int e = (int)(amax_bits >> 23);
+  if (e == 255) return 255u;
+  int b = e - Fmt<FMT>::emax;
+  return b < 0 ? 0u : (unsigned)b;
+}
+
+// The scale operand of the scaled conversions: an fp32 whose exponent field
+// is the E8M0 byte.
+__device__ __forceinline__ float scale_operand(unsigned sb) { return __uint_as_float(sb << 23); }
+
+// bf16 bits of 448 * 2^(sb-127) = 1.75 * 2^(sb-119), replicated in both
+// halves: the FP8 saturation bound for a pair of bf16 magnitudes.
+__device__ __forceinline__ unsigned e4m3_clamp_bf16x2(unsigned sb) {
+  unsigned c = ((sb + 8u) << 7) | 0x60u;
+  return c | (c << 16);
+}
+
+// Clamp the magnitudes of two packed bf16 values to c (bits), keeping signs.
+__device__ __forceinline__ unsigned clamp_bf16x2(unsigned w, unsigned c2) {
+  u16x2 m = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
+  m = __builtin_elementwise_min(m, __builtin_bit_cast(u16x2, c2));
+  return (w & 0x80008000u) | __builtin_bit_cast(unsigned, m);
+}
+
+// Clamp an fp32 magnitude to c, keeping the sign.
+__device__ __forceinline__ float clamp_f32(float y, float c) {
+  float m = __builtin_fminf(__builtin_fabsf(y), c);
+  return __builtin_copysignf(m, y);
+}
+
+// ---- conversions of 8 bf16 (one 16-byte piece) -------------------------
+
+// An empty asm that hides a value from the optimizer.  The ROCm 7.2 middle
+// end folds calls of the bf16-source FP4 conversion intrinsic as if their
+// result did not depend on the source (distinct calls are merged into one);
+// passing each source through this barrier keeps them apart.  It emits no
+// instruction.
+__device__ __forceinline__ unsigned opaque(unsigned v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+// E2M1: 8 nibbles, element 2k in the low nibble of byte k.
+__device__ __forceinline__ unsigned fp4_from_bf16x8(u32x4 w, float sc) {
+  unsigned c = 0;
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(bf16x2, opaque(w.x)), sc, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(bf16x2, opaque(w.y)), sc, 1);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(bf16x2, opaque(w.z)), sc, 2);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(bf16x2, opaque(w.w)), sc, 3);
+  return c;
+}
+
+__device__ __forceinline__ u32x4 bf16x8_from_fp4(unsigned c, float sc) {
+  u32x4 o;
+  o.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 0));
+  o.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 1));
+  o.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 2));
+  o.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 3));
+  return o;
+}
+
+// E4M3: 8 bytes, element k in byte k; w must already be clamped.
+__device__ __forceinline__ unsigned fp8_pair_word(unsigned lo_pair, unsigned hi_pair, float sc) {
+  i16x2 c = {0, 0};
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(c, __builtin_bit_cast(bf16x2, lo_pair), sc, false);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(c, __builtin_bit_cast(bf16x2, hi_pair), sc, true);
+  return __builtin_bit_cast(unsigned, c);
+}
+
+__device__ __forceinline__ u32x2 fp8_from_bf16x8(u32x4 w, float sc) {
+  u32x2 c;
+  c.x = fp8_pair_word(w.x, w.y, sc);
+  c.y = fp8_pair_word(w.z, w.w, sc);
+  return c;
+}
+
+__device__ __forceinline__ u32x4 bf16x8_from_fp8(u32x2 c, float sc) {
+  u32x4 o;
+  o.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, false));
+  o.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, true));
+  o.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, false));
+  o.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, true));
+  return o;
+}
+
+// ---- conversions of fp32 pairs (rotated values) ---------------------------
+
+// Two fp32 -> one byte of two E2M1 nibbles at byte position SEL of `old`.
+template <int SEL>
+__device__ __forceinline__ unsigned fp4_from_f32x2(unsigned old, float a, float b, float sc) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, sc, SEL);
+}
+
+// Two fp32 -> two E4M3 bytes in the low (HI=false) or high half of `old`;
+// the inputs must already be clamped.
+template <bool HI>
+__device__ __forceinline__ unsigned fp8_from_f32x2(unsigned old, float a, float b, float sc) {
+  i16x2 c = __builtin_bit_cast(i16x2, old);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, a, b, sc, HI);
+  return __builtin_bit_cast(unsigned, c);
+}
+
+// ---- software element steps (exact in fp32) ------------------------------
+
+// Element value of a magnitude code times 2^s (exact in fp32: at most 4
+// significant bits, exponent >= -136).
+template <int FMT>
+__device__ __forceinline__ float decode_mag(unsigned mag, int s) {
+  using F = Fmt<FMT>;
+  unsigned ef = mag >> F::mbits;
+  unsigned m = mag & ((1u << F::mbits) - 1u);
+  int mant = ef ? (int)(m | (1u << F::mbits)) : (int)m;
+  int ex = (ef ? (int)ef : 1) - F::bias - F::mbits;
+  return __builtin_amdgcn_ldexpf((float)mant, ex + s);
+}
+
+// Signed code -> fp32 value times 2^s (NaN for the E4M3 NaN code).
+template <int FMT>
+__device__ __forceinline__ float decode_code(unsigned code, int s) {
+  using F = Fmt<FMT>;
+  unsigned mag = code & (F::sign_bit - 1u);
+  if (FMT == 1 && mag == 0x7Fu) return __uint_as_float(F32_NAN);
+  float v = decode_mag<FMT>(mag, s);
+  return (code & F::sign_bit) ? -v : v;
+}
+
+// fp32 -> bf16 bits, round to nearest-even (finite or infinite inputs).
+__device__ __forceinline__ unsigned bf16_rne(float f) {
+  unsigned u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---- cross-lane helpers ---------------------------------------------------
+
+// DPP controls (gfx9 encodings).
+enum : int {
+  DPP_QUAD_1032 = 0xB1,  // quad_perm [1,0,3,2]
+  DPP_QUAD_2301 = 0x4E,  // quad_perm [2,3,0,1]
+  DPP_ROW_ROR4 = 0x124,
+  DPP_ROW_ROR8 = 0x128,
+  DPP_ROW_HALF_MIRROR = 0x141,
+};
+
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ unsigned umax(unsigned a, unsigned b) { return a > b ? a : b; }
+
+// Max of v over lanes l and l^32 (v_permlane32_swap exchanges the upper
+// half-wave of its first operand with the lower half-wave of its second).
+__device__ __forceinline__ unsigned max_across_halves(unsigned v) {
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return umax(r[0], r[1]);
+}
+
+// Half-wave exchange (one v_permlane32_swap).  After the call:
+//   lanes l < 32:  a = a[l],      b = a[l + 32]
+//   lanes l >= 32: a = b[l - 32], b = b[l]
+// i.e. the upper half's `a` and the lower half's `b` trade places.
+__device__ __forceinline__ void swap_halves(unsigned &a, unsigned &b) {
+  auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+}  // namespace mx

@@ -68,6 +68,8 @@ def lib():
         L.orc_encode.restype = i32
         L.orc_decode.argtypes = [i32, i32]
         L.orc_decode.restype = ctypes.c_double
+        L.orc_scale_exponent_n.argtypes = [i32, vp, i64, vp]
+        L.orc_scale_exponent_n.restype = None
         L.orc_encode_n.argtypes = [i32, vp, vp, i64, vp]
         L.orc_encode_n.restype = None
         L.orc_qdq_value_n.argtypes = [i32, vp, vp, i64, vp]
@@ -140,6 +142,13 @@ def encode(fmt: int, y: float, s: int) -> int:
 
 def decode(fmt: int, code: int) -> float:
     return lib().orc_decode(fmt, int(code))
+
+
+def scale_exponent_n(fmt: int, amax: np.ndarray) -> np.ndarray:
+    amax = np.ascontiguousarray(amax, dtype=np.float64)
+    out = np.empty(amax.shape, dtype=np.int32)
+    lib().orc_scale_exponent_n(fmt, _ptr(amax), amax.size, _ptr(out))
+    return out
 
 
 def encode_n(fmt: int, y: np.ndarray, s: np.ndarray) -> np.ndarray:

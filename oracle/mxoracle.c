@@ -202,6 +202,12 @@ double orc_decode(int fmt, int code)
     return sign ? -v : v;
 }
 
+void orc_scale_exponent_n(int fmt, const double *amax, int64_t n, int32_t *s)
+{
+    for (int64_t i = 0; i < n; ++i)
+        s[i] = orc_scale_exponent(fmt, amax[i]);
+}
+
 void orc_encode_n(int fmt, const double *y, const int32_t *s, int64_t n,
                   uint8_t *codes)
 {

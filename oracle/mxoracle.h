@@ -74,8 +74,10 @@ int orc_encode(int fmt, double y, int s);
 double orc_decode(int fmt, int code);
 
 /* Batch forms of the element steps, for exhaustive pins and band checks:
+ * s[i]     = orc_scale_exponent(fmt, amax[i]);
  * codes[i] = orc_encode(fmt, y[i], s[i]);
  * q[i]     = orc_decode(fmt, orc_encode(fmt, y[i], s[i])) * 2^s[i]. */
+void orc_scale_exponent_n(int fmt, const double *amax, int64_t n, int32_t *s);
 void orc_encode_n(int fmt, const double *y, const int32_t *s, int64_t n,
                   uint8_t *codes);
 void orc_qdq_value_n(int fmt, const double *y, const int32_t *s, int64_t n,

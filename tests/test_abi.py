@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any GPU work (CPU only: no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmxqdq.h")
+LIB = os.path.join(ROOT, "microscaling_quantize_dequantize_amd", "libmxqdq.so")
+
+MX_OK, MX_EFMT, MX_EDTYPE, MX_ESHAPE, MX_EROT, MX_ENULL, MX_EALIGN, MX_ELAUNCH = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from microscaling_quantize_dequantize_amd import build
+        build.build()
+    L = ctypes.CDLL(LIB)
+    vp, i64, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.mx_qdq.argtypes = [i, vp, i, i64, i64, vp, i, vp]
+    L.mx_quantize.argtypes = [i, vp, i64, i64, vp, i, vp, vp]
+    L.mx_dequantize.argtypes = [i, vp, vp, i64, i64, i, vp]
+    L.mx_rotate.argtypes = [vp, i, i64, i64, vp, i, vp]
+    L.mx_set_stream.argtypes = [vp]
+    L.mx_get_stream.restype = vp
+    L.mx_status_string.argtypes = [i]
+    L.mx_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"MX_API\s+[\w\s\*]+?\b(mx_\w+)\s*\(", text)
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_symbols())
+    assert {"mx_qdq", "mx_quantize", "mx_dequantize", "mx_rotate", "mx_set_stream",
+            "mx_get_stream", "mx_status_string"} <= names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_header_compiles_as_c():
+    import subprocess
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        open(src, "w").write('#include "libmxqdq.h"\nint main(void){return MX_OK;}\n')
+        subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                               "-c", src, "-o", os.path.join(d, "t.o")])
+
+
+A = 1 << 20  # a 16-byte aligned fake address; never dereferenced (validation fails first)
+
+
+def test_qdq_argument_errors(lib):
+    q = lib.mx_qdq
+    assert q(2, A, 0, 4, 64, None, 0, A) == MX_EFMT
+    assert q(-1, A, 0, 4, 64, None, 0, A) == MX_EFMT
+    assert q(0, A, 2, 4, 64, None, 0, A) == MX_EDTYPE
+    assert q(0, A, 0, 4, 48, None, 0, A) == MX_ESHAPE
+    assert q(0, A, 0, -1, 64, None, 0, A) == MX_ESHAPE
+    assert q(0, A, 0, 4, -32, None, 0, A) == MX_ESHAPE
+    assert q(0, A, 0, 1 << 40, 1 << 20, None, 0, A) == MX_ESHAPE
+    assert q(0, A, 0, 4, 64, A, 8, A) == MX_EROT
+    assert q(0, A, 0, 4, 64, A, 256, A) == MX_EROT
+    assert q(0, A, 0, 4, 96, A, 64, A) == MX_EROT      # K % r != 0
+    assert q(0, A, 0, 4, 64, None, 16, A) == MX_EROT   # NULL matrix
+    assert q(0, None, 0, 4, 64, None, 0, A) == MX_ENULL
+    assert q(0, A, 0, 4, 64, None, 0, None) == MX_ENULL
+    assert q(0, A + 8, 0, 4, 64, None, 0, A) == MX_EALIGN
+    assert q(0, A, 0, 4, 64, None, 0, A + 2) == MX_EALIGN
+    assert q(0, A, 0, 4, 64, A + 4, 16, A) == MX_EALIGN
+
+
+def test_quantize_argument_errors(lib):
+    q = lib.mx_quantize
+    assert q(5, A, 4, 64, None, 0, A, A) == MX_EFMT
+    assert q(0, A, 4, 33, None, 0, A, A) == MX_ESHAPE
+    assert q(0, A, 4, 64, A, 12, A, A) == MX_EROT
+    assert q(0, A, 4, 64, None, 0, None, A) == MX_ENULL
+    assert q(0, A, 4, 64, None, 0, A, None) == MX_ENULL
+    assert q(0, A, 4, 64, None, 0, A + 4, A) == MX_EALIGN
+    assert q(1, A, 4, 64, None, 0, A, A + 2) == MX_EALIGN
+
+
+def test_dequantize_and_rotate_argument_errors(lib):
+    assert lib.mx_dequantize(3, A, A, 4, 64, 0, A) == MX_EFMT
+    assert lib.mx_dequantize(0, A, A, 4, 64, 7, A) == MX_EDTYPE
+    assert lib.mx_dequantize(0, A, A, 4, 40, 0, A) == MX_ESHAPE
+    assert lib.mx_dequantize(0, None, A, 4, 64, 0, A) == MX_ENULL
+    assert lib.mx_dequantize(0, A, A, 4, 64, 0, A + 8) == MX_EALIGN
+    assert lib.mx_rotate(A, 0, 4, 64, A, 0, A) == MX_EROT  # rotation is required
+    assert lib.mx_rotate(A, 3, 4, 64, A, 16, A) == MX_EDTYPE
+    assert lib.mx_rotate(A, 0, 4, 64, A, 16, None) == MX_ENULL
+
+
+def test_empty_is_a_noop(lib):
+    # no pointer is touched and no kernel is launched for M == 0 or K == 0
+    assert lib.mx_qdq(0, None, 0, 0, 64, None, 0, None) == MX_OK
+    assert lib.mx_qdq(1, None, 1, 5, 0, None, 0, None) == MX_OK
+    assert lib.mx_quantize(0, None, 0, 128, None, 0, None, None) == MX_OK
+    assert lib.mx_dequantize(1, None, None, 0, 32, 0, None) == MX_OK
+    assert lib.mx_rotate(None, 0, 0, 128, A, 128, None) == MX_OK
+
+
+def test_status_strings_and_stream(lib):
+    for code in (MX_OK, MX_EFMT, MX_EDTYPE, MX_ESHAPE, MX_EROT, MX_ENULL, MX_EALIGN, MX_ELAUNCH):
+        s = lib.mx_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.mx_status_string(-99).decode() == "unknown status"
+    lib.mx_set_stream(ctypes.c_void_p(0x1234))
+    assert lib.mx_get_stream() == 0x1234
+    lib.mx_set_stream(None)
+    assert not lib.mx_get_stream()
+
+
+def test_library_does_not_reference_the_oracle():
+    """The product library links nothing from oracle/ (no orc_ symbols)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", LIB], capture_output=True, text=True).stdout
+    assert "orc_" not in out

@@ -1,0 +1,200 @@
+"""GPU parity of the rotated path (runtime rotation on MFMA, then MX).
+
+Exact where the rotation itself is exact (identity, signed permutations,
+diagonal matrices); otherwise within the stated band: rotated values within
+beta = 1e-5 * sum|x R|, and at most 0.01% of elements differing from the
+oracle, each only where a value within beta would round differently."""
+import numpy as np
+import pytest
+
+import oracle
+from _parity import (E2M1, E4M3, THREADS, assert_bits_equal, band_check, bf16_values, bits_of,
+                     rotate_within_beta, to_gpu_bf16, to_gpu_f32, unpack_codes)
+from microscaling_quantize_dequantize_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+RS = [16, 32, 64, 128]
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from microscaling_quantize_dequantize_amd import binding
+    return binding
+
+
+def no_negative_zero(x):
+    """An exactly rotated zero is +0 (IEEE sum), while the unrotated path keeps
+    -0; bit-exact comparisons across the two use inputs without -0."""
+    x = x.copy()
+    x[x == 0x8000] = 0
+    return x
+
+
+def bf16_exact(v):
+    f = np.asarray(v, dtype=np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(v, dtype=np.float64))
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("r", RS)
+def test_rotate_step_within_tolerance(mx, r):
+    import torch
+    rng = np.random.default_rng(r)
+    x = W.generate("c3", rows=(0, 64))[:, :4096]
+    for R in (W.hadamard_rotation(r), W.f32_to_bf16_bits(rng.standard_normal((r, r)).astype(np.float32))):
+        yg = mx.mx_rotate(to_gpu_bf16(x), to_gpu_bf16(R))
+        torch.cuda.synchronize()
+        y, beta = oracle.rotate(x, R, r, threads=THREADS)
+        rotate_within_beta(bits_of(yg).view(np.float32), y, beta)
+    xf = W.random_f32((32, 2048), seed=r)
+    Rf = rng.standard_normal((r, r)).astype(np.float32)
+    yg = mx.mx_rotate(to_gpu_f32(xf), to_gpu_f32(Rf))
+    torch.cuda.synchronize()
+    y, beta = oracle.rotate(xf, Rf, r)
+    rotate_within_beta(bits_of(yg).view(np.float32), y, beta)
+
+
+@pytest.mark.parametrize("r", RS)
+def test_identity_rotation_is_bit_exact(mx, r):
+    import torch
+    x = no_negative_zero(W.generate("c5a", rows=(0, 64)))
+    xg = to_gpu_bf16(x)
+    I = to_gpu_bf16(bf16_exact(np.eye(r)))
+    for fmt in (E2M1, E4M3):
+        a = mx.mx_qdq(fmt, xg, rot=I)
+        b = mx.mx_qdq(fmt, xg)
+        ca, sa = mx.mx_quantize(fmt, xg, rot=I)
+        torch.cuda.synchronize()
+        assert_bits_equal(bits_of(a), bits_of(b), f"identity r={r} fmt{fmt}")
+        c_ref, s_ref = oracle.quantize(fmt, x, threads=THREADS)
+        assert_bits_equal(bits_of(sa), s_ref, "identity scales")
+        assert_bits_equal(bits_of(ca), c_ref, "identity codes")
+
+
+@pytest.mark.parametrize("r", RS)
+def test_exact_rotations_are_bit_exact(mx, r):
+    """Signed permutations and diagonal matrices make y exact in fp32, so the
+    GPU must match the oracle bit for bit (this also pins the fp32 inputs of
+    the hardware conversions)."""
+    import torch
+    rng = np.random.default_rng(300 + r)
+    x = no_negative_zero(W.generate("c5a", rows=(64, 128))[:, :4096])
+    perm = rng.permutation(r)
+    P = np.zeros((r, r))
+    P[np.arange(r), perm] = rng.choice([-1.0, 1.0], size=r)
+    D = np.diag(W.bf16_bits_to_f32(W.f32_to_bf16_bits(
+        (rng.uniform(0.5, 2.0, size=r) * rng.choice([-1, 1], size=r)).astype(np.float32))).astype(np.float64))
+    for R in (P, D):
+        Rb = bf16_exact(R)
+        for fmt in (E2M1, E4M3):
+            out = mx.mx_qdq(fmt, to_gpu_bf16(x), rot=to_gpu_bf16(Rb))
+            codes, scales = mx.mx_quantize(fmt, to_gpu_bf16(x), rot=to_gpu_bf16(Rb))
+            torch.cuda.synchronize()
+            assert_bits_equal(bits_of(out), oracle.qdq(fmt, x, Rb, r, threads=THREADS), f"exact R r={r}")
+            c_ref, s_ref = oracle.quantize(fmt, x, Rb, r, threads=THREADS)
+            assert_bits_equal(bits_of(scales), s_ref, "exact R scales")
+            assert_bits_equal(bits_of(codes), c_ref, "exact R codes")
+
+
+def _qdq_band(mx, fmt, x, R, r, rows=None, xg=None):
+    import torch
+    out = mx.mx_qdq(fmt, to_gpu_bf16(x) if xg is None else xg, rot=to_gpu_bf16(R))
+    torch.cuda.synchronize()
+    if rows is not None:
+        out = out[torch.from_numpy(rows).cuda()]
+        x = x[rows]
+    y, beta = oracle.rotate(np.ascontiguousarray(x), R, r, threads=THREADS)
+    return band_check(fmt, y, beta, deq_gpu=bf16_values(bits_of(out)))
+
+
+def _quant_band(mx, fmt, x, R, r, rows=None, xg=None):
+    import torch
+    codes, scales = mx.mx_quantize(fmt, to_gpu_bf16(x) if xg is None else xg, rot=to_gpu_bf16(R))
+    torch.cuda.synchronize()
+    if rows is not None:
+        idx = torch.from_numpy(rows).cuda()
+        codes, scales, x = codes[idx], scales[idx], x[rows]
+    y, beta = oracle.rotate(np.ascontiguousarray(x), R, r, threads=THREADS)
+    return band_check(fmt, y, beta, codes_gpu=unpack_codes(fmt, bits_of(codes), x.shape[1]),
+                      scales_gpu=bits_of(scales))
+
+
+def sample_rows(M, seed):
+    """The first and last 64-row blocks plus three random ones."""
+    rng = np.random.default_rng(seed)
+    blocks = sorted({0, M // 64 - 1, *rng.choice(M // 64, size=3, replace=False).tolist()})
+    return np.concatenate([np.arange(b * 64, b * 64 + 64) for b in blocks])
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+@pytest.mark.parametrize("r", RS)
+def test_hadamard_small_shapes(mx, fmt, r):
+    for shape in [(3, 128), (7, 384), (33, 1024 + 128)]:
+        x = W.random_bf16(shape, seed=shape[0] + r)
+        R = W.hadamard_rotation(r)
+        _qdq_band(mx, fmt, x, R, r)
+        _quant_band(mx, fmt, x, R, r)
+
+
+def test_c3_mxfp4_qdq_rot32(mx):
+    x = W.generate("c3")
+    stats = _qdq_band(mx, E2M1, x, W.hadamard_rotation(32), 32)
+    print("c3", stats)
+
+
+def test_c4_mxfp4_quantize_rot128(mx):
+    import torch
+    x = W.generate("c4")
+    R = W.hadamard_rotation(128)
+    xg, Rg = to_gpu_bf16(x), to_gpu_bf16(R)
+    stats = _quant_band(mx, E2M1, x, R, 128, rows=sample_rows(x.shape[0], 4), xg=xg)
+    print("c4", stats)
+    # property at full size: rotated QDQ == dequantize(rotated quantize)
+    codes, scales = mx.mx_quantize(E2M1, xg, rot=Rg)
+    d = mx.mx_dequantize(E2M1, codes, scales, x.shape[1])
+    q = mx.mx_qdq(E2M1, xg, rot=Rg)
+    assert torch.equal(d.view(torch.int16), q.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,rs", [("c5a", (16, 64)), ("c5b", (16, 64, 128)), ("c5c", (16, 64))])
+def test_c5_layers_rotated(mx, name, rs):
+    """Full-size launch; the oracle checks a sample of row blocks (including
+    the first and the last) and the full tensors are checked for
+    qdq == dequantize(quantize)."""
+    import torch
+    x = W.generate(name)
+    rows = sample_rows(x.shape[0], len(name))
+    xg = to_gpu_bf16(x)
+    for r in rs:
+        R = W.hadamard_rotation(r)
+        Rg = to_gpu_bf16(R)
+        for fmt in (E2M1, E4M3):
+            stats = _qdq_band(mx, fmt, x, R, r, rows=rows, xg=xg)
+            print(name, r, fmt, stats)
+            codes, scales = mx.mx_quantize(fmt, xg, rot=Rg)
+            d = mx.mx_dequantize(fmt, codes, scales, x.shape[1])
+            q = mx.mx_qdq(fmt, xg, rot=Rg)
+            assert torch.equal(d.view(torch.int16), q.view(torch.int16))
+            del codes, scales, d, q
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+@pytest.mark.parametrize("r", RS)
+def test_fp32_source_rotated(mx, fmt, r):
+    import torch
+    rng = np.random.default_rng(500 + r)
+    x = W.random_f32((48, 1024), seed=r)
+    R = (W.sylvester_hadamard(r) / np.sqrt(r)).astype(np.float32)
+    out = mx.mx_qdq(fmt, to_gpu_f32(x), rot=to_gpu_f32(R))
+    torch.cuda.synchronize()
+    y, beta = oracle.rotate(x, R, r)
+    band_check(fmt, y, beta, deq_gpu=bits_of(out).view(np.float32).astype(np.float64), dst_bf16=False)
+    Pm = np.zeros((r, r), dtype=np.float32)
+    Pm[np.arange(r), rng.permutation(r)] = 1.0
+    out = mx.mx_qdq(fmt, to_gpu_f32(x), rot=to_gpu_f32(Pm))
+    torch.cuda.synchronize()
+    assert_bits_equal(bits_of(out), oracle.qdq(fmt, x, Pm, r), "f32 permutation")
