@@ -1,0 +1,236 @@
+"""Benchmark of the MX quantize-dequantize hot path on one MI355X.
+
+One step = one pass of the whole path over the resident 8192 x 57344 bf16
+layer (the largest Llama-3.1-70B layer shape the pages benchmark, read as
+M x K; values N(0, 0.02^2) with 1/1024 subnormal-range and 1/1024
+saturating groups):
+  mx_qdq      MXFP4 and MXFP8, rotation none / 16 / 64 / 128 (normalised
+              Hadamard, bf16), bf16 out                       -- 8 launches
+  mx_quantize MXFP4 and MXFP8, rotation none / 128, codes + E8M0 scales
+                                                               -- 4 launches
+value = algorithmic bytes of the step / step time (GB = 1e9 B).  Algorithmic
+bytes per element: QDQ 2 + 2; quantize 2 + 0.5 + 1/32 (MXFP4) or 2 + 1 + 1/32
+(MXFP8); the rotation matrix (<= 32 KiB) is not counted.
+
+Each launch is bracketed by HIP events on the stream it runs on (the binding
+launches on torch's current stream); the roofline entry uses the average
+launch duration of the kernel with the largest share of the step.  A plain
+device copy of the layer is timed the same way as a measured copy ceiling.
+The CPU baseline runs the oracle (unchanged) on a bounded row sample of the
+same layer and variants, on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0
+METRIC = "effective HBM GB/s (and % of MI355X peak) for MXFP4/MXFP8 QDQ per layer"
+WORKLOAD = "c5b"
+
+
+def variants():
+    out = []
+    for fmt in (0, 1):
+        for r in (0, 16, 64, 128):
+            out.append(("qdq", fmt, r))
+    for fmt in (0, 1):
+        for r in (0, 128):
+            out.append(("quantize", fmt, r))
+    return out
+
+
+def bytes_per_element(op, fmt):
+    if op == "qdq":
+        return 4.0
+    return 2.0 + (0.5 if fmt == 0 else 1.0) + 1.0 / 32.0
+
+
+def name_of(op, fmt, r):
+    return f"{op}_{'mxfp4' if fmt == 0 else 'mxfp8'}_rot{r}"
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "microscaling_quantize_dequantize_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_name):
+    """HBM traffic per launch from the committed counter summary, if it was
+    taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("kernels", {}).get(kernel_name)
+
+
+def cpu_baseline(x_bits, rots, rows):
+    import numpy as np
+
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    sample = np.ascontiguousarray(x_bits[:rows])
+    n = sample.size
+    total_bytes = 0.0
+    t0 = time.perf_counter()
+    for op, fmt, r in variants():
+        R = rots[r][0] if r else None
+        if op == "qdq":
+            oracle.qdq(fmt, sample, R, r, threads=threads)
+        else:
+            oracle.quantize(fmt, sample, R, r, threads=threads)
+        total_bytes += n * bytes_per_element(op, fmt)
+    dt = time.perf_counter() - t0
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0-{rows - 1} of the 8192x57344 layer ({n} elements), all 12 step variants, "
+                      f"{dt:.1f} s wall", "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the MX QDQ path shards by rows with no exchange, "
+              "and this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from microscaling_quantize_dequantize_amd import binding as mx
+    from microscaling_quantize_dequantize_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    x_bits = W.generate(WORKLOAD)
+    M, K = x_bits.shape
+    n = M * K
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    rots = {}
+    for r in (16, 64, 128):
+        Rb = W.hadamard_rotation(r)
+        rots[r] = (Rb, torch.from_numpy(Rb.view(np.int16)).view(torch.bfloat16).to(dev))
+    dst = torch.empty_like(x)
+    codes = {0: torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+             1: torch.empty((M, K), dtype=torch.uint8, device=dev)}
+    scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    copy_dst = torch.empty_like(x)
+
+    var = variants()
+
+    def launch(op, fmt, r):
+        R = rots[r][1] if r else None
+        if op == "qdq":
+            mx.mx_qdq(fmt, x, rot=R, dst=dst)
+        else:
+            mx.mx_quantize(fmt, x, rot=R, codes=codes[fmt], scales=scales)
+
+    def step(events=None):
+        for i, v in enumerate(var):
+            if events is not None:
+                events[i][0].record()
+            launch(*v)
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+        copy_dst.copy_(x)
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in var]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # measured copy ceiling: device-to-device copy of the same layer
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in cev:
+        a.record()
+        copy_dst.copy_(x)
+        b.record()
+    torch.cuda.synchronize()
+    copy_ms = float(np.mean([a.elapsed_time(b) for a, b in cev]))
+    copy_gbps = 2 * n * 2 / (copy_ms * 1e-3) / 1e9
+
+    per = []
+    step_bytes = 0.0
+    for i, (op, fmt, r) in enumerate(var):
+        ms = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        avg = float(np.mean(ms))
+        b = n * bytes_per_element(op, fmt)
+        step_bytes += b
+        per.append({"kernel": name_of(op, fmt, r), "bytes": int(b), "avg_us": round(avg * 1e3, 2),
+                    "min_us": round(min(ms) * 1e3, 2), "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+                    "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4),
+                    "frac_of_copy": round(b / (avg * 1e-3) / 1e9 / copy_gbps, 4),
+                    "elements_per_s": round(n / (avg * 1e-3), 1)})
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes / (wall / args.steps) / 1e9
+    dom = max(per, key=lambda p: p["avg_us"])
+    achieved = dom["bytes"] / (dom["avg_us"] * 1e-6) / 1e9
+    by = {p["kernel"]: p for p in per}
+    ratio = {f"rot128_over_rot0_{f}": round(by[f"qdq_{f}_rot128"]["avg_us"] / by[f"qdq_{f}_rot0"]["avg_us"], 3)
+             for f in ("mxfp4", "mxfp8")}
+    ratio.update({f"quantize_rot128_over_rot0_{f}": round(
+        by[f"quantize_{f}_rot128"]["avg_us"] / by[f"quantize_{f}_rot0"]["avg_us"], 3) for f in ("mxfp4", "mxfp8")})
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "8192x57344 bf16 layer, N(0,0.02^2) with subnormal-range and saturating "
+                               "groups: MXFP4+MXFP8 QDQ (rotation none/16/64/128) and quantize "
+                               "(rotation none/128)",
+                   "M": M, "K": K, "launches_per_step": len(var), "bytes_per_step": int(step_bytes),
+                   "copy_ceiling_GBps": round(copy_gbps, 1),
+                   "value_frac_of_peak": round(value / PEAK_GBPS, 4)},
+        "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": round(achieved, 1),
+                     "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": load_traffic(dom["kernel"])},
+        "variants": per,
+        "ratios": ratio,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(x_bits, rots, args.cpu_rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

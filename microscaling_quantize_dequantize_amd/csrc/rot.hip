@@ -6,7 +6,7 @@
 // Every r-chunk x of a row becomes y = x . R (y[j] = sum_t x[t] R[t][j]).
 //
 // Since K is a multiple of r and of 32, chunks never straddle rows and the
-// matrix is one flat array of r-chunks.  The kernel works on blocks of
+// matrix is one flat array of r-chunks.  The kernels work on blocks of
 // RB = max(r, 32) elements with the block-diagonal matrix diag(R, ..., R) of
 // size RB (r = 16 gives diag(R, R)), so that every 32-group lies inside one
 // block.
@@ -16,19 +16,26 @@
 //   A (32 x 16) = a 32-column slice jt of Reff^T, staged once per workgroup in
 //                 LDS in the exact order the MFMAs read it;
 //   B (16 x 32) = 32 consecutive blocks ("a tile"), lane l holding block l%32.
-// The k index of an MFMA is free to permute as long as A and B agree, so lane
-// l reads the half (l/32) of its block as RB/16 contiguous 16-byte loads:
-// k-step kb covers t = (l/32)*RB/2 + 8*kb + i, i = 0..7.
+// The k index of an MFMA is free to permute as long as A and B agree: k-step
+// kb covers t = 16*kb + 8*(l/32) + i (i = 0..7).
 // In the 32x32 accumulator, lane l holds, for its block, the 16 values
 // j = 32*jt + 8q + 4*(l/32) + e (q, e = 0..3): one 32-group (jt) is split
-// between lanes l and l+32, so its abs-max takes one v_permlane32_swap.  The
-// same swap then trades 4-element runs so that each lane stores 16-byte runs.
+// between lanes l and l+32, so its abs-max takes one v_permlane32_swap, and
+// the same swap then trades 4-element runs so that each lane owns whole
+// 16-byte pieces of output.
+//
+// Memory traffic: a lane of the MFMA layout touches one block, so reading or
+// writing HBM in that layout scatters every instruction over 32 blocks.
+// Instead each wave stages its tile through a private LDS buffer: the input
+// is read from HBM fully coalesced (lane l, instruction q: 16-byte piece
+// 64q + l of the tile), written to LDS, and read back in the MFMA layout; the
+// outputs go the opposite way.  Pieces are placed with an XOR swizzle of
+// their column so that both the linear and the per-block accesses are free
+// of bank conflicts.
 #include "launch.h"
 #include "mx_device.h"
 
 namespace mx {
-
-constexpr int RTHREADS = 256;
 
 // Entry (t, j) of the block-diagonal RB x RB matrix built from the r x r R.
 template <typename T>
@@ -37,30 +44,37 @@ __device__ __forceinline__ T reff(const T *__restrict__ rot, int r, int t, int j
   return rot[(t % r) * r + (j % r)];
 }
 
-// Store a lane's share of one rotated, quantized 32-group.
-//   acc[4q + e] = y[32*jt + 8q + 4h + e] of block `blk` (h = lane / 32).
-template <int FMT, int OP, int RB, bool SRC_BF16>
-__device__ __forceinline__ void group_epilogue(const f32x16 &acc, int64_t blk, int jt, int h,
-                                               bool valid, void *__restrict__ dst,
-                                               uint8_t *__restrict__ codes, unsigned &sbw) {
-  const int64_t e0 = blk * RB + jt * 32;  // first element of the group
-  if (OP == OP_ROTATE) {
-    if (valid) {
-      float *d = (float *)dst + e0 + 4 * h;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        __builtin_nontemporal_store(f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]},
-                                    (f32x4 *)(d + 8 * q));
-    }
-    return;
-  }
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// LDS slot of 16-byte piece p of a tile whose blocks hold C pieces each: the
+// low 3 bits of the piece index are XORed with bits of the block index so
+// that eight consecutive blocks at the same column land in eight different
+// 16-byte bank groups, and eight consecutive pieces stay a permutation of
+// one aligned group of eight.
+template <int C>
+__device__ __forceinline__ int swz(int p) {
+  constexpr int SH = C >= 8 ? ilog2(C) : 3;
+  constexpr int MK = (C < 8 ? C : 8) - 1;
+  return p ^ ((p >> SH) & MK);
+}
+
+// Orders a wave's LDS accesses around an exchange between its lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The MX step of one rotated 32-group held as acc[4q + e] =
+// y[32*jt + 8q + 4h + e] by lanes l and l+32: scale byte, scale operand and
+// the 4-element runs' codes c[q] (E2M1: 16 bits, E4M3: 32 bits).
+template <int FMT>
+__device__ __forceinline__ void group_codes(const f32x16 &acc, unsigned &sb, float &sc, unsigned c[4]) {
   unsigned m = 0;
 #pragma unroll
   for (int a = 0; a < 16; ++a) m = umax(m, __float_as_uint(acc[a]) & 0x7FFFFFFFu);
   m = max_across_halves(m);
-  const unsigned sb = scale_byte<FMT>(m);
-  const float sc = scale_operand(sb);
-  sbw |= sb << (8 * jt);
+  sb = scale_byte<FMT>(m);
+  sc = scale_operand(sb);
   float y[16];
 #pragma unroll
   for (int a = 0; a < 16; ++a) y[a] = acc[a];
@@ -69,8 +83,6 @@ __device__ __forceinline__ void group_epilogue(const f32x16 &acc, int64_t blk, i
 #pragma unroll
     for (int a = 0; a < 16; ++a) y[a] = clamp_f32(y[a], cl);
   }
-  // c[q]: the run's 4 codes (E2M1: 16 bits, E4M3: 32 bits)
-  unsigned c[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (FMT == 0) {
@@ -81,84 +93,80 @@ __device__ __forceinline__ void group_epilogue(const f32x16 &acc, int64_t blk, i
       c[q] = fp8_from_f32x2<true>(v, y[4 * q + 2], y[4 * q + 3], sc);
     }
   }
-  if (OP == OP_QDQ && SRC_BF16) {
-    unsigned o[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (FMT == 0) {
-        o[2 * q] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[q], sc, 0));
-        o[2 * q + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[q], sc, 1));
-      } else {
-        o[2 * q] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[q], sc, false));
-        o[2 * q + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[q], sc, true));
-      }
-    }
-    if (sb == 255u) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] = BF16_NAN | (BF16_NAN << 16);
-    }
-    // runs (0,1) and (2,3): lower half ends with j 0-7 / 16-23, upper 8-15 / 24-31
-    swap_halves(o[0], o[2]);
-    swap_halves(o[1], o[3]);
-    swap_halves(o[4], o[6]);
-    swap_halves(o[5], o[7]);
-    if (valid) {
-      u32x4 *d = (u32x4 *)((uint16_t *)dst + e0 + 8 * h);
-      __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, d);
-      __builtin_nontemporal_store(u32x4{o[4], o[5], o[6], o[7]}, d + 2);
-    }
-  } else if (OP == OP_QDQ) {  // fp32 destination: exact software decode
-    const int s = (int)sb - 127;
-    constexpr int CB = FMT == 0 ? 4 : 8;
-    constexpr unsigned CM = (1u << CB) - 1u;
-    if (valid) {
-      float *d = (float *)dst + e0 + 4 * h;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[e] = sb == 255u ? __uint_as_float(F32_NAN) : decode_code<FMT>((c[q] >> (CB * e)) & CM, s);
-        __builtin_nontemporal_store(v, (f32x4 *)(d + 8 * q));
-      }
-    }
-  } else {  // quantize: codes
-    if (FMT == 0) {
-      // byte pairs: lower lane holds codes of j 0-3|8-11 (ca) and 16-19|24-27
-      // (cb); the upper lane the runs 4 elements later.
-      unsigned ca = c[0] | (c[1] << 16), cb = c[2] | (c[3] << 16);
-      if (sb == 255u) ca = cb = 0u;
-      swap_halves(ca, cb);
-      // lower: ca = bytes {0-1, 4-5}, cb = {2-3, 6-7}; upper: {8-9,12-13}, {10-11,14-15}
-      const unsigned w0 = (ca & 0xFFFFu) | (cb << 16);
-      const unsigned w1 = (ca >> 16) | (cb & 0xFFFF0000u);
-      if (valid) __builtin_nontemporal_store(u32x2{w0, w1}, (u32x2 *)(codes + e0 / 2 + 8 * h));
-    } else {
-      unsigned r0 = c[0], r1 = c[1], r2 = c[2], r3 = c[3];
-      if (sb == 255u) r0 = r1 = r2 = r3 = 0x7F7F7F7Fu;
-      swap_halves(r0, r1);  // lower: bytes 0-7,  upper: 8-15
-      swap_halves(r2, r3);  // lower: bytes 16-23, upper: 24-31
-      swap_halves(r0, r2);  // lower: 0-3, 8-11 -> with r1/r3 below: 0-15
-      swap_halves(r1, r3);
-      // lower now holds bytes 0-3 (r0), 4-7 (r1), 8-11 (r2), 12-15 (r3);
-      // upper holds 16-19, 20-23, 24-27, 28-31.
-      if (valid) __builtin_nontemporal_store(u32x4{r0, r1, r2, r3}, (u32x4 *)(codes + e0 + 16 * h));
-    }
-  }
 }
 
-template <int FMT, int OP, int RB>
-__global__ __launch_bounds__(RTHREADS) void k_rot_bf16(const uint16_t *__restrict__ src,
-                                                       const uint16_t *__restrict__ rot, int r,
-                                                       void *__restrict__ dst,
-                                                       uint8_t *__restrict__ codes,
-                                                       uint8_t *__restrict__ scales,
-                                                       int64_t n_blk) {
-  constexpr int NJT = RB / 32, NKB = RB / 16, HALF = RB / 2;
+// Dequantized bf16 of one group, rearranged across the lane pair: on return
+// the lower lane holds elements 0-7 (o[0..3]) and 16-23 (o[4..7]) of the
+// group, the upper lane 8-15 and 24-31.
+template <int FMT>
+__device__ __forceinline__ void group_bf16(const unsigned c[4], unsigned sb, float sc, unsigned o[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (FMT == 0) {
+      o[2 * q] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[q], sc, 0));
+      o[2 * q + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[q], sc, 1));
+    } else {
+      o[2 * q] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[q], sc, false));
+      o[2 * q + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[q], sc, true));
+    }
+  }
+  if (sb == 255u) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = BF16_NAN | (BF16_NAN << 16);
+  }
+  swap_halves(o[0], o[2]);
+  swap_halves(o[1], o[3]);
+  swap_halves(o[4], o[6]);
+  swap_halves(o[5], o[7]);
+}
+
+// E2M1 codes of one group: on return the lower lane holds bytes 0-7 of the
+// group's 16 code bytes (w[0], w[1]), the upper lane bytes 8-15.
+__device__ __forceinline__ void group_fp4_bytes(const unsigned c[4], unsigned sb, unsigned w[2]) {
+  // before the swap the lower lane holds the codes of j 0-3|8-11 (ca) and
+  // 16-19|24-27 (cb), the upper lane those 4 elements later
+  unsigned ca = c[0] | (c[1] << 16), cb = c[2] | (c[3] << 16);
+  if (sb == 255u) ca = cb = 0u;
+  swap_halves(ca, cb);
+  // lower: ca = bytes {0-1, 4-5}, cb = {2-3, 6-7}; upper: {8-9, 12-13}, {10-11, 14-15}
+  w[0] = (ca & 0xFFFFu) | (cb << 16);
+  w[1] = (ca >> 16) | (cb & 0xFFFF0000u);
+}
+
+// E4M3 codes of one group: on return the lower lane holds bytes 0-15 of the
+// group's 32 code bytes, the upper lane bytes 16-31.
+__device__ __forceinline__ void group_fp8_bytes(const unsigned c[4], unsigned sb, unsigned r[4]) {
+  r[0] = c[0];
+  r[1] = c[1];
+  r[2] = c[2];
+  r[3] = c[3];
+  if (sb == 255u) r[0] = r[1] = r[2] = r[3] = 0x7F7F7F7Fu;
+  swap_halves(r[0], r[1]);  // lower: bytes 0-7,  upper: 8-15
+  swap_halves(r[2], r[3]);  // lower: bytes 16-23, upper: 24-31
+  swap_halves(r[0], r[2]);  // lower: 0-3 | 8-11, upper: 16-19 | 24-27
+  swap_halves(r[1], r[3]);  // lower: 4-7 | 12-15, upper: 20-23 | 28-31
+}
+
+// bf16 source, OP_QDQ (bf16 out) or OP_QUANT, staged through LDS.
+template <int FMT, int OP, int RB, int THREADS>
+__global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict__ src,
+                                                      const uint16_t *__restrict__ rot, int r,
+                                                      void *__restrict__ dst, uint8_t *__restrict__ codes,
+                                                      uint8_t *__restrict__ scales, int64_t n_blk) {
+  constexpr int NJT = RB / 32, NKB = RB / 16;
+  constexpr int C = RB / 8;           // 16-byte input pieces per block
+  constexpr int TP = 32 * C;          // input pieces per tile (= 64 * NKB)
+  constexpr int WAVES = THREADS / 64;
+  constexpr int C4 = RB / 32;         // E2M1 code pieces per block
+  constexpr int C8 = RB / 16;         // E4M3 code pieces per block
   __shared__ u32x4 sA[NJT * NKB * 64];
-  for (int idx = threadIdx.x; idx < NJT * NKB * 64; idx += RTHREADS) {
+  __shared__ u32x4 sT[WAVES][TP];
+
+  // A fragment (jt, kb) of lane ln: Reff[t][j] for j = 32*jt + ln%32 and
+  // t = 16*kb + 8*(ln/32) + i, i = 0..7.
+  for (int idx = threadIdx.x; idx < NJT * NKB * 64; idx += THREADS) {
     const int ln = idx & 63, f = idx >> 6, jt = f / NKB, kb = f % NKB;
-    const int j = jt * 32 + (ln & 31), t0 = (ln >> 5) * HALF + 8 * kb;
+    const int j = jt * 32 + (ln & 31), t0 = 16 * kb + 8 * (ln >> 5);
     unsigned w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -167,17 +175,34 @@ __global__ __launch_bounds__(RTHREADS) void k_rot_bf16(const uint16_t *__restric
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, h = lane >> 5;
-  const int waves = RTHREADS / 64;
+  const int lane = threadIdx.x & 63, h = lane >> 5, n = lane & 31;
+  u32x4 *T = sT[threadIdx.x >> 6];
+  const int64_t n_elem = n_blk * RB;
   const int64_t n_tiles = (n_blk + 31) / 32;
-  for (int64_t tile = (int64_t)blockIdx.x * waves + (threadIdx.x >> 6); tile < n_tiles;
-       tile += (int64_t)gridDim.x * waves) {
-    const int64_t blk = tile * 32 + (lane & 31);
-    const bool valid = blk < n_blk;
-    const u32x4 *p = (const u32x4 *)(src + blk * RB + h * HALF);
+  const int64_t stride = (int64_t)gridDim.x * WAVES;
+  for (int64_t tile = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); tile < n_tiles; tile += stride) {
+    const int64_t e_tile = tile * 32 * RB;  // first element of the tile
+    // 1. coalesced loads of the tile into LDS
+    {
+      const u32x4 *g = (const u32x4 *)(src + e_tile);
+      u32x4 v[NKB];
+#pragma unroll
+      for (int q = 0; q < NKB; ++q) {
+        const int p = q * 64 + lane;
+        v[q] = e_tile + (int64_t)p * 8 < n_elem ? __builtin_nontemporal_load(g + p) : u32x4{0u, 0u, 0u, 0u};
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int q = 0; q < NKB; ++q) T[swz<C>(q * 64 + lane)] = v[q];
+      wave_lds_sync();
+    }
+    // 2. B fragments in the MFMA layout
     u32x4 b[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) b[kb] = valid ? __builtin_nontemporal_load(p + kb) : u32x4{0u, 0u, 0u, 0u};
+    for (int kb = 0; kb < NKB; ++kb) b[kb] = T[swz<C>(n * C + 2 * kb + h)];
+    wave_lds_sync();
+    // 3. rotate, quantize, and place the outputs in LDS
+    const int64_t blk = tile * 32 + n;
     unsigned sbw = 0;
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) {
@@ -186,35 +211,150 @@ __global__ __launch_bounds__(RTHREADS) void k_rot_bf16(const uint16_t *__restric
       for (int kb = 0; kb < NKB; ++kb)
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sA[(jt * NKB + kb) * 64 + lane]),
                                                       __builtin_bit_cast(bf16x8, b[kb]), acc, 0, 0, 0);
-      group_epilogue<FMT, OP, RB, true>(acc, blk, jt, h, valid, dst, codes, sbw);
+      unsigned sb, c[4];
+      float sc;
+      group_codes<FMT>(acc, sb, sc, c);
+      sbw |= sb << (8 * jt);
+      if (OP == OP_QDQ) {
+        unsigned o[8];
+        group_bf16<FMT>(c, sb, sc, o);
+        T[swz<C>(n * C + 4 * jt + h)] = u32x4{o[0], o[1], o[2], o[3]};
+        T[swz<C>(n * C + 4 * jt + 2 + h)] = u32x4{o[4], o[5], o[6], o[7]};
+      } else if (FMT == 0) {
+        unsigned w[2];
+        group_fp4_bytes(c, sb, w);
+        ((u32x2 *)T)[2 * swz<C4>(n * C4 + jt) + h] = u32x2{w[0], w[1]};
+      } else {
+        unsigned w[4];
+        group_fp8_bytes(c, sb, w);
+        T[swz<C8>(n * C8 + 2 * jt + h)] = u32x4{w[0], w[1], w[2], w[3]};
+      }
     }
-    if (OP == OP_QUANT && h == 0 && valid) {
+    if (OP == OP_QUANT && h == 0 && blk < n_blk) {
       if (NJT == 4) *(unsigned *)(scales + blk * 4) = sbw;
       else if (NJT == 2) *(uint16_t *)(scales + blk * 2) = (uint16_t)sbw;
       else scales[blk] = (uint8_t)sbw;
     }
+    wave_lds_sync();
+    // 4. coalesced stores of the tile's outputs
+    if (OP == OP_QDQ) {
+      u32x4 *g = (u32x4 *)((uint16_t *)dst + e_tile);
+#pragma unroll
+      for (int q = 0; q < NKB; ++q) {
+        const int p = q * 64 + lane;
+        const u32x4 v = T[swz<C>(p)];
+        if (e_tile + (int64_t)p * 8 < n_elem) __builtin_nontemporal_store(v, g + p);
+      }
+    } else {
+      constexpr int CP = FMT == 0 ? C4 : C8;      // code pieces per block
+      constexpr int EPP = FMT == 0 ? 32 : 16;     // elements per code piece
+      u32x4 *g = (u32x4 *)(codes + e_tile / EPP * 16);
+#pragma unroll
+      for (int q = 0; q < (32 * CP + 63) / 64; ++q) {
+        const int p = q * 64 + lane;
+        if (p < 32 * CP) {
+          const u32x4 v = T[swz<CP>(p)];
+          if (e_tile + (int64_t)p * EPP < n_elem) __builtin_nontemporal_store(v, g + p);
+        }
+      }
+    }
+    wave_lds_sync();
   }
 }
 
-// fp32 source: v_mfma_f32_32x32x2_f32, lane l supplying B[k = l/32][n = l%32]
-// and A[m = l%32][k = l/32]; k-step kb covers t = (l/32)*RB/2 + kb.
+// The rotation alone (fp32 out) or fp32 sources: direct stores.
+// For bf16 sources the B layout is the one above; for fp32 sources
+// v_mfma_f32_32x32x2_f32 takes one value per lane: lane l supplies
+// B[k = l/32][n = l%32] and A[m = l%32][k = l/32], and k-step kb covers
+// t = (l/32)*RB/2 + kb.
 template <int FMT, int OP, int RB>
-__global__ __launch_bounds__(RTHREADS) void k_rot_f32(const float *__restrict__ src,
+__device__ __forceinline__ void store_direct(const f32x16 &acc, int64_t blk, int jt, int h, bool valid,
+                                             void *__restrict__ dst) {
+  const int64_t e0 = blk * RB + jt * 32;
+  float *d = (float *)dst + e0 + 4 * h;
+  if (OP == OP_ROTATE) {
+    if (valid) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_nontemporal_store(f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]},
+                                    (f32x4 *)(d + 8 * q));
+    }
+    return;
+  }
+  // fp32 QDQ: exact software decode of the hardware codes
+  unsigned sb, c[4];
+  float sc;
+  group_codes<FMT>(acc, sb, sc, c);
+  const int s = (int)sb - 127;
+  constexpr int CB = FMT == 0 ? 4 : 8;
+  constexpr unsigned CM = (1u << CB) - 1u;
+  if (valid) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = sb == 255u ? __uint_as_float(F32_NAN) : decode_code<FMT>((c[q] >> (CB * e)) & CM, s);
+      __builtin_nontemporal_store(v, (f32x4 *)(d + 8 * q));
+    }
+  }
+}
+
+constexpr int DTHREADS = 256;
+
+template <int RB>
+__global__ __launch_bounds__(DTHREADS) void k_rotate_bf16(const uint16_t *__restrict__ src,
+                                                          const uint16_t *__restrict__ rot, int r,
+                                                          float *__restrict__ dst, int64_t n_blk) {
+  constexpr int NJT = RB / 32, NKB = RB / 16;
+  __shared__ u32x4 sA[NJT * NKB * 64];
+  for (int idx = threadIdx.x; idx < NJT * NKB * 64; idx += DTHREADS) {
+    const int ln = idx & 63, f = idx >> 6, jt = f / NKB, kb = f % NKB;
+    const int j = jt * 32 + (ln & 31), t0 = 16 * kb + 8 * (ln >> 5);
+    unsigned w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (unsigned)reff(rot, r, t0 + 2 * i, j) | ((unsigned)reff(rot, r, t0 + 2 * i + 1, j) << 16);
+    sA[idx] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  const int64_t n_tiles = (n_blk + 31) / 32;
+  for (int64_t tile = (int64_t)blockIdx.x * (DTHREADS / 64) + (threadIdx.x >> 6); tile < n_tiles;
+       tile += (int64_t)gridDim.x * (DTHREADS / 64)) {
+    const int64_t blk = tile * 32 + (lane & 31);
+    const bool valid = blk < n_blk;
+    const u32x4 *p = (const u32x4 *)(src + blk * RB) + h;
+    u32x4 b[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) b[kb] = valid ? __builtin_nontemporal_load(p + 2 * kb) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sA[(jt * NKB + kb) * 64 + lane]),
+                                                      __builtin_bit_cast(bf16x8, b[kb]), acc, 0, 0, 0);
+      store_direct<0, OP_ROTATE, RB>(acc, blk, jt, h, valid, dst);
+    }
+  }
+}
+
+template <int FMT, int OP, int RB>
+__global__ __launch_bounds__(DTHREADS) void k_rot_f32(const float *__restrict__ src,
                                                       const float *__restrict__ rot, int r,
                                                       void *__restrict__ dst, int64_t n_blk) {
   constexpr int NJT = RB / 32, HALF = RB / 2;
   __shared__ float sA[NJT * HALF * 64];
-  for (int idx = threadIdx.x; idx < NJT * HALF * 64; idx += RTHREADS) {
+  for (int idx = threadIdx.x; idx < NJT * HALF * 64; idx += DTHREADS) {
     const int ln = idx & 63, f = idx >> 6, jt = f / HALF, kb = f % HALF;
     sA[idx] = reff(rot, r, (ln >> 5) * HALF + kb, jt * 32 + (ln & 31));
   }
   __syncthreads();
-
   const int lane = threadIdx.x & 63, h = lane >> 5;
-  const int waves = RTHREADS / 64;
   const int64_t n_tiles = (n_blk + 31) / 32;
-  for (int64_t tile = (int64_t)blockIdx.x * waves + (threadIdx.x >> 6); tile < n_tiles;
-       tile += (int64_t)gridDim.x * waves) {
+  for (int64_t tile = (int64_t)blockIdx.x * (DTHREADS / 64) + (threadIdx.x >> 6); tile < n_tiles;
+       tile += (int64_t)gridDim.x * (DTHREADS / 64)) {
     const int64_t blk = tile * 32 + (lane & 31);
     const bool valid = blk < n_blk;
     const f32x4 *p = (const f32x4 *)(src + blk * RB + h * HALF);
@@ -227,65 +367,76 @@ __global__ __launch_bounds__(RTHREADS) void k_rot_f32(const float *__restrict__ 
       xv[4 * k4 + 2] = v[2];
       xv[4 * k4 + 3] = v[3];
     }
-    unsigned sbw = 0;
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) {
       f32x16 acc = {};
 #pragma unroll
       for (int kb = 0; kb < HALF; ++kb)
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[(jt * HALF + kb) * 64 + lane], xv[kb], acc, 0, 0, 0);
-      group_epilogue<FMT, OP, RB, false>(acc, blk, jt, h, valid, dst, nullptr, sbw);
+      store_direct<FMT, OP, RB>(acc, blk, jt, h, valid, dst);
     }
   }
 }
 
-template <int FMT, int OP, int RB>
-static void run_bf16(const void *src, const void *rot, int r, void *dst, uint8_t *codes,
-                     uint8_t *scales, int64_t n, unsigned grid_cap, hipStream_t st) {
-  const int64_t n_blk = n / RB;
-  const int64_t tiles = (n_blk + 31) / 32;
-  int64_t g = (tiles + 3) / 4;
-  if (g > grid_cap) g = grid_cap;
-  k_rot_bf16<FMT, OP, RB><<<(unsigned)g, RTHREADS, 0, st>>>((const uint16_t *)src, (const uint16_t *)rot, r,
-                                                           dst, codes, scales, n_blk);
+// Workgroup size of the staged kernels: enough waves per CU to cover the
+// HBM latency within the LDS budget (A fragments RB*RB*2 bytes per
+// workgroup plus a 64*RB-byte tile buffer per wave).
+template <int RB> struct StagedCfg;
+template <> struct StagedCfg<32> { static constexpr int threads = 256, per_cu = 8; };
+template <> struct StagedCfg<64> { static constexpr int threads = 512, per_cu = 3; };
+template <> struct StagedCfg<128> { static constexpr int threads = 768, per_cu = 1; };
+
+static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
+  int64_t g = (tiles + waves - 1) / waves;
+  const int64_t cap = (int64_t)device_cu_count() * per_cu;
+  return (unsigned)(g < cap ? g : cap);
 }
 
 template <int FMT, int OP, int RB>
-static void run_f32(const void *src, const void *rot, int r, void *dst, int64_t n, unsigned grid_cap,
-                    hipStream_t st) {
+static void run_staged(const void *src, const void *rot, int r, void *dst, uint8_t *codes, uint8_t *scales,
+                       int64_t n, hipStream_t st) {
+  using Cfg = StagedCfg<RB>;
   const int64_t n_blk = n / RB;
-  const int64_t tiles = (n_blk + 31) / 32;
-  int64_t g = (tiles + 3) / 4;
-  if (g > grid_cap) g = grid_cap;
-  k_rot_f32<FMT, OP, RB><<<(unsigned)g, RTHREADS, 0, st>>>((const float *)src, (const float *)rot, r, dst, n_blk);
+  const unsigned g = persistent_grid((n_blk + 31) / 32, Cfg::threads / 64, Cfg::per_cu);
+  k_rot_bf16<FMT, OP, RB, Cfg::threads><<<g, Cfg::threads, 0, st>>>(
+      (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk);
+}
+
+template <int FMT, int OP, int RB>
+static void run_direct(int dtype, const void *src, const void *rot, int r, void *dst, int64_t n, hipStream_t st) {
+  const int64_t n_blk = n / RB;
+  const unsigned g = persistent_grid((n_blk + 31) / 32, DTHREADS / 64, 8);
+  if (dtype == 0)
+    k_rotate_bf16<RB><<<g, DTHREADS, 0, st>>>((const uint16_t *)src, (const uint16_t *)rot, r, (float *)dst, n_blk);
+  else
+    k_rot_f32<FMT, OP, RB><<<g, DTHREADS, 0, st>>>((const float *)src, (const float *)rot, r, dst, n_blk);
 }
 
 template <int FMT, int OP>
 static void dispatch_rb(int dtype, const void *src, const void *rot, int r, void *dst, uint8_t *codes,
-                        uint8_t *scales, int64_t n, unsigned cap, hipStream_t st) {
+                        uint8_t *scales, int64_t n, hipStream_t st) {
   const int rb = r < 32 ? 32 : r;
-  if (dtype == 0) {
-    if (rb == 32) run_bf16<FMT, OP, 32>(src, rot, r, dst, codes, scales, n, cap, st);
-    else if (rb == 64) run_bf16<FMT, OP, 64>(src, rot, r, dst, codes, scales, n, cap, st);
-    else run_bf16<FMT, OP, 128>(src, rot, r, dst, codes, scales, n, cap, st);
+  if (dtype == 0 && OP != OP_ROTATE) {
+    if (rb == 32) run_staged<FMT, OP, 32>(src, rot, r, dst, codes, scales, n, st);
+    else if (rb == 64) run_staged<FMT, OP, 64>(src, rot, r, dst, codes, scales, n, st);
+    else run_staged<FMT, OP, 128>(src, rot, r, dst, codes, scales, n, st);
   } else if (OP != OP_QUANT) {
-    if (rb == 32) run_f32<FMT, OP, 32>(src, rot, r, dst, n, cap, st);
-    else if (rb == 64) run_f32<FMT, OP, 64>(src, rot, r, dst, n, cap, st);
-    else run_f32<FMT, OP, 128>(src, rot, r, dst, n, cap, st);
+    if (rb == 32) run_direct<FMT, OP, 32>(dtype, src, rot, r, dst, n, st);
+    else if (rb == 64) run_direct<FMT, OP, 64>(dtype, src, rot, r, dst, n, st);
+    else run_direct<FMT, OP, 128>(dtype, src, rot, r, dst, n, st);
   }
 }
 
 hipError_t launch_rot(int fmt, int op, int dtype, const void *src, const void *rot, int r, void *dst,
                       uint8_t *codes, uint8_t *scales, int64_t n, hipStream_t st) {
-  const unsigned cap = (unsigned)device_cu_count() * 8u;
   if (op == OP_ROTATE) {
-    dispatch_rb<0, OP_ROTATE>(dtype, src, rot, r, dst, codes, scales, n, cap, st);
+    dispatch_rb<0, OP_ROTATE>(dtype, src, rot, r, dst, codes, scales, n, st);
   } else if (fmt == 0) {
-    if (op == OP_QDQ) dispatch_rb<0, OP_QDQ>(dtype, src, rot, r, dst, codes, scales, n, cap, st);
-    else dispatch_rb<0, OP_QUANT>(dtype, src, rot, r, dst, codes, scales, n, cap, st);
+    if (op == OP_QDQ) dispatch_rb<0, OP_QDQ>(dtype, src, rot, r, dst, codes, scales, n, st);
+    else dispatch_rb<0, OP_QUANT>(dtype, src, rot, r, dst, codes, scales, n, st);
   } else {
-    if (op == OP_QDQ) dispatch_rb<1, OP_QDQ>(dtype, src, rot, r, dst, codes, scales, n, cap, st);
-    else dispatch_rb<1, OP_QUANT>(dtype, src, rot, r, dst, codes, scales, n, cap, st);
+    if (op == OP_QDQ) dispatch_rb<1, OP_QDQ>(dtype, src, rot, r, dst, codes, scales, n, st);
+    else dispatch_rb<1, OP_QUANT>(dtype, src, rot, r, dst, codes, scales, n, st);
   }
   return hipGetLastError();
 }
