@@ -180,22 +180,33 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
   const int64_t n_elem = n_blk * RB;
   const int64_t n_tiles = (n_blk + 31) / 32;
   const int64_t stride = (int64_t)gridDim.x * WAVES;
-  for (int64_t tile = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); tile < n_tiles; tile += stride) {
-    const int64_t e_tile = tile * 32 * RB;  // first element of the tile
-    // 1. coalesced loads of the tile into LDS
-    {
-      const u32x4 *g = (const u32x4 *)(src + e_tile);
-      u32x4 v[NKB];
+
+  // Coalesced loads of one tile: piece 64q + lane.  Full tiles (all but
+  // possibly the last one) skip the per-piece bound (a wave-uniform test).
+  auto load_tile = [&](int64_t tile, u32x4 *v) {
+    const int64_t e_tile = tile * 32 * RB;
+    const u32x4 *g = (const u32x4 *)(src + e_tile) + lane;
+    if (e_tile + (int64_t)TP * 8 <= n_elem) {
 #pragma unroll
-      for (int q = 0; q < NKB; ++q) {
-        const int p = q * 64 + lane;
-        v[q] = e_tile + (int64_t)p * 8 < n_elem ? __builtin_nontemporal_load(g + p) : u32x4{0u, 0u, 0u, 0u};
-      }
-      wave_lds_sync();
+      for (int q = 0; q < NKB; ++q) v[q] = __builtin_nontemporal_load(g + q * 64);
+    } else {
 #pragma unroll
-      for (int q = 0; q < NKB; ++q) T[swz<C>(q * 64 + lane)] = v[q];
-      wave_lds_sync();
+      for (int q = 0; q < NKB; ++q)
+        v[q] = e_tile + (int64_t)(q * 64 + lane) * 8 < n_elem ? __builtin_nontemporal_load(g + q * 64)
+                                                             : u32x4{0u, 0u, 0u, 0u};
     }
+  };
+
+  int64_t tile = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
+  u32x4 v[NKB];
+  if (tile < n_tiles) load_tile(tile, v);
+  for (; tile < n_tiles; tile += stride) {
+    const int64_t e_tile = tile * 32 * RB;  // first element of the tile
+    const bool full = e_tile + (int64_t)TP * 8 <= n_elem;
+    // 1. the tile into LDS
+#pragma unroll
+    for (int q = 0; q < NKB; ++q) T[swz<C>(q * 64 + lane)] = v[q];
+    wave_lds_sync();
     // 2. B fragments in the MFMA layout
     u32x4 b[NKB];
 #pragma unroll
@@ -211,23 +222,25 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
       for (int kb = 0; kb < NKB; ++kb)
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sA[(jt * NKB + kb) * 64 + lane]),
                                                       __builtin_bit_cast(bf16x8, b[kb]), acc, 0, 0, 0);
-      unsigned sb, c[4];
-      float sc;
-      group_codes<FMT>(acc, sb, sc, c);
-      sbw |= sb << (8 * jt);
-      if (OP == OP_QDQ) {
-        unsigned o[8];
-        group_bf16<FMT>(c, sb, sc, o);
-        T[swz<C>(n * C + 4 * jt + h)] = u32x4{o[0], o[1], o[2], o[3]};
-        T[swz<C>(n * C + 4 * jt + 2 + h)] = u32x4{o[4], o[5], o[6], o[7]};
-      } else if (FMT == 0) {
-        unsigned w[2];
-        group_fp4_bytes(c, sb, w);
-        ((u32x2 *)T)[2 * swz<C4>(n * C4 + jt) + h] = u32x2{w[0], w[1]};
-      } else {
-        unsigned w[4];
-        group_fp8_bytes(c, sb, w);
-        T[swz<C8>(n * C8 + 2 * jt + h)] = u32x4{w[0], w[1], w[2], w[3]};
+      {
+        unsigned sb, c[4];
+        float sc;
+        group_codes<FMT>(acc, sb, sc, c);
+        sbw |= sb << (8 * jt);
+        if (OP == OP_QDQ) {
+          unsigned o[8];
+          group_bf16<FMT>(c, sb, sc, o);
+          T[swz<C>(n * C + 4 * jt + h)] = u32x4{o[0], o[1], o[2], o[3]};
+          T[swz<C>(n * C + 4 * jt + 2 + h)] = u32x4{o[4], o[5], o[6], o[7]};
+        } else if (FMT == 0) {
+          unsigned w[2];
+          group_fp4_bytes(c, sb, w);
+          ((u32x2 *)T)[2 * swz<C4>(n * C4 + jt) + h] = u32x2{w[0], w[1]};
+        } else {
+          unsigned w[4];
+          group_fp8_bytes(c, sb, w);
+          T[swz<C8>(n * C8 + 2 * jt + h)] = u32x4{w[0], w[1], w[2], w[3]};
+        }
       }
     }
     if (OP == OP_QUANT && h == 0 && blk < n_blk) {
@@ -238,27 +251,34 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
     wave_lds_sync();
     // 4. coalesced stores of the tile's outputs
     if (OP == OP_QDQ) {
-      u32x4 *g = (u32x4 *)((uint16_t *)dst + e_tile);
+      u32x4 *g = (u32x4 *)((uint16_t *)dst + e_tile) + lane;
+      u32x4 o[NKB];
 #pragma unroll
-      for (int q = 0; q < NKB; ++q) {
-        const int p = q * 64 + lane;
-        const u32x4 v = T[swz<C>(p)];
-        if (e_tile + (int64_t)p * 8 < n_elem) __builtin_nontemporal_store(v, g + p);
+      for (int q = 0; q < NKB; ++q) o[q] = T[swz<C>(q * 64 + lane)];
+      if (full) {
+#pragma unroll
+        for (int q = 0; q < NKB; ++q) __builtin_nontemporal_store(o[q], g + q * 64);
+      } else {
+#pragma unroll
+        for (int q = 0; q < NKB; ++q)
+          if (e_tile + (int64_t)(q * 64 + lane) * 8 < n_elem) __builtin_nontemporal_store(o[q], g + q * 64);
       }
     } else {
       constexpr int CP = FMT == 0 ? C4 : C8;      // code pieces per block
       constexpr int EPP = FMT == 0 ? 32 : 16;     // elements per code piece
-      u32x4 *g = (u32x4 *)(codes + e_tile / EPP * 16);
+      constexpr int NQ = (32 * CP + 63) / 64;
+      u32x4 *g = (u32x4 *)(codes + e_tile / EPP * 16) + lane;
+      u32x4 o[NQ];
 #pragma unroll
-      for (int q = 0; q < (32 * CP + 63) / 64; ++q) {
+      for (int q = 0; q < NQ; ++q) o[q] = (q * 64 + lane < 32 * CP) ? T[swz<CP>(q * 64 + lane)] : u32x4{};
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
         const int p = q * 64 + lane;
-        if (p < 32 * CP) {
-          const u32x4 v = T[swz<CP>(p)];
-          if (e_tile + (int64_t)p * EPP < n_elem) __builtin_nontemporal_store(v, g + p);
-        }
+        if (p < 32 * CP && (full || e_tile + (int64_t)p * EPP < n_elem)) __builtin_nontemporal_store(o[q], g + q * 64);
       }
     }
     wave_lds_sync();
+    if (tile + stride < n_tiles) load_tile(tile + stride, v);
   }
 }
 
@@ -378,13 +398,14 @@ __global__ __launch_bounds__(DTHREADS) void k_rot_f32(const float *__restrict__ 
   }
 }
 
-// Workgroup size of the staged kernels: enough waves per CU to cover the
-// HBM latency within the LDS budget (A fragments RB*RB*2 bytes per
-// workgroup plus a 64*RB-byte tile buffer per wave).
+// Launch shape of the staged kernels: workgroup size and workgroups per CU
+// in the grid.  LDS per workgroup is RB*RB*2 bytes of A fragments plus a
+// 64*RB-byte tile buffer per wave.  Chosen by measurement on MI355X (8192 x
+// 57344 bf16, QDQ and quantize); the persistent grid amortises the A staging.
 template <int RB> struct StagedCfg;
-template <> struct StagedCfg<32> { static constexpr int threads = 256, per_cu = 8; };
-template <> struct StagedCfg<64> { static constexpr int threads = 512, per_cu = 3; };
-template <> struct StagedCfg<128> { static constexpr int threads = 768, per_cu = 1; };
+template <> struct StagedCfg<32> { static constexpr int threads = 1024, per_cu = 8; };
+template <> struct StagedCfg<64> { static constexpr int threads = 512, per_cu = 8; };
+template <> struct StagedCfg<128> { static constexpr int threads = 256, per_cu = 2; };
 
 static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
   int64_t g = (tiles + waves - 1) / waves;

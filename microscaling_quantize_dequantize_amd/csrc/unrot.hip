@@ -9,16 +9,18 @@
 // 4 consecutive lanes hold one group and a wave reads 1 KiB of contiguous
 // input per instruction.  The group abs-max is reduced in registers (packed
 // u16 max on sign-cleared bits) and then across the 4 lanes with two DPP
-// quad permutations; no LDS is touched.  Each thread keeps UNROLL pieces in
-// flight before converting them.
+// quad permutations; no LDS is touched.
+//
+// Launch shape (measured on MI355X, 8192 x 57344 bf16): small blocks of 128
+// threads, one block per 128*UNROLL pieces and no persistent loop, stream
+// HBM best -- QDQ with one piece per thread, quantize with two.  The grid
+// is capped only for inputs beyond 2^22 blocks, which then loop.
 #include "launch.h"
 #include "mx_device.h"
 
 namespace mx {
 
-constexpr int THREADS = 256;
-constexpr int UNROLL = 4;
-constexpr int64_t SWEEP = THREADS * UNROLL;  // pieces per block per sweep
+constexpr int64_t MAX_BLOCKS = (int64_t)1 << 22;
 
 __device__ __forceinline__ u32x4 load_piece(const u32x4 *p) { return __builtin_nontemporal_load(p); }
 
@@ -33,12 +35,13 @@ __device__ __forceinline__ unsigned piece_amax_bf16(u32x4 w) {
 }
 
 // OP_QDQ: dst (bf16) = dequantized values.  OP_QUANT: codes + scales.
-template <int FMT, int OP>
+template <int FMT, int OP, int THREADS, int UNROLL>
 __global__ __launch_bounds__(THREADS) void k_unrot_bf16(const u32x4 *__restrict__ src,
                                                         u32x4 *__restrict__ dst,
                                                         uint8_t *__restrict__ codes,
                                                         uint8_t *__restrict__ scales,
                                                         int64_t n_pieces) {
+  constexpr int64_t SWEEP = THREADS * UNROLL;  // pieces per block per sweep
   const int tid = threadIdx.x;
   for (int64_t sweep = blockIdx.x; sweep * SWEEP < n_pieces; sweep += gridDim.x) {
     const int64_t base = sweep * SWEEP + tid;
@@ -104,9 +107,10 @@ __global__ __launch_bounds__(THREADS) void k_unrot_bf16(const u32x4 *__restrict_
 }
 
 // fp32 source, QDQ only: one 16-byte piece = 4 elements, 8 lanes per group.
-template <int FMT>
+template <int FMT, int THREADS, int UNROLL>
 __global__ __launch_bounds__(THREADS) void k_unrot_f32(const u32x4 *__restrict__ src,
                                                        u32x4 *__restrict__ dst, int64_t n_pieces) {
+  constexpr int64_t SWEEP = THREADS * UNROLL;
   const int tid = threadIdx.x;
   for (int64_t sweep = blockIdx.x; sweep * SWEEP < n_pieces; sweep += gridDim.x) {
     const int64_t base = sweep * SWEEP + tid;
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(THREADS) void k_unrot_f32(const u32x4 *__restrict__
 }
 
 // Dequantize: one lane per 8 elements (a quarter group).
-template <int FMT, int DT>
+template <int FMT, int DT, int THREADS>
 __global__ __launch_bounds__(THREADS) void k_dequant(const uint8_t *__restrict__ codes,
                                                      const uint8_t *__restrict__ scales,
                                                      void *__restrict__ dst, int64_t n_pieces) {
@@ -194,31 +198,36 @@ __global__ __launch_bounds__(THREADS) void k_dequant(const uint8_t *__restrict__
   }
 }
 
-static unsigned sweep_grid(int64_t n_pieces) {
-  const int64_t want = (n_pieces + SWEEP - 1) / SWEEP;
-  const int64_t cap = (int64_t)device_cu_count() * 8;
-  return (unsigned)(want < cap ? want : cap);
+static unsigned grid_for(int64_t n_pieces, int64_t per_block) {
+  const int64_t want = (n_pieces + per_block - 1) / per_block;
+  return (unsigned)(want < MAX_BLOCKS ? want : MAX_BLOCKS);
 }
+
+// Launch shapes: threads per block and pieces per thread.
+constexpr int QDQ_T = 128, QDQ_U = 1;
+constexpr int QNT_T = 128, QNT_U = 2;
+constexpr int DEQ_T = 128;
 
 hipError_t launch_unrot(int fmt, int op, int dtype, const void *src, void *dst, uint8_t *codes,
                         uint8_t *scales, int64_t n, hipStream_t stream) {
   const u32x4 *s = (const u32x4 *)src;
   if (dtype == 1) {  // fp32, QDQ only
     const int64_t np = n / 4;
-    const unsigned g = sweep_grid(np);
-    if (fmt == 0) k_unrot_f32<0><<<g, THREADS, 0, stream>>>(s, (u32x4 *)dst, np);
-    else k_unrot_f32<1><<<g, THREADS, 0, stream>>>(s, (u32x4 *)dst, np);
+    const unsigned g = grid_for(np, QDQ_T * QDQ_U);
+    if (fmt == 0) k_unrot_f32<0, QDQ_T, QDQ_U><<<g, QDQ_T, 0, stream>>>(s, (u32x4 *)dst, np);
+    else k_unrot_f32<1, QDQ_T, QDQ_U><<<g, QDQ_T, 0, stream>>>(s, (u32x4 *)dst, np);
     return hipGetLastError();
   }
   const int64_t np = n / 8;
-  const unsigned g = sweep_grid(np);
   u32x4 *d = (u32x4 *)dst;
   if (op == OP_QDQ) {
-    if (fmt == 0) k_unrot_bf16<0, OP_QDQ><<<g, THREADS, 0, stream>>>(s, d, nullptr, nullptr, np);
-    else k_unrot_bf16<1, OP_QDQ><<<g, THREADS, 0, stream>>>(s, d, nullptr, nullptr, np);
+    const unsigned g = grid_for(np, QDQ_T * QDQ_U);
+    if (fmt == 0) k_unrot_bf16<0, OP_QDQ, QDQ_T, QDQ_U><<<g, QDQ_T, 0, stream>>>(s, d, nullptr, nullptr, np);
+    else k_unrot_bf16<1, OP_QDQ, QDQ_T, QDQ_U><<<g, QDQ_T, 0, stream>>>(s, d, nullptr, nullptr, np);
   } else {
-    if (fmt == 0) k_unrot_bf16<0, OP_QUANT><<<g, THREADS, 0, stream>>>(s, nullptr, codes, scales, np);
-    else k_unrot_bf16<1, OP_QUANT><<<g, THREADS, 0, stream>>>(s, nullptr, codes, scales, np);
+    const unsigned g = grid_for(np, QNT_T * QNT_U);
+    if (fmt == 0) k_unrot_bf16<0, OP_QUANT, QNT_T, QNT_U><<<g, QNT_T, 0, stream>>>(s, nullptr, codes, scales, np);
+    else k_unrot_bf16<1, OP_QUANT, QNT_T, QNT_U><<<g, QNT_T, 0, stream>>>(s, nullptr, codes, scales, np);
   }
   return hipGetLastError();
 }
@@ -226,15 +235,13 @@ hipError_t launch_unrot(int fmt, int op, int dtype, const void *src, void *dst, 
 hipError_t launch_dequant(int fmt, int dtype, const uint8_t *codes, const uint8_t *scales,
                           void *dst, int64_t n, hipStream_t stream) {
   const int64_t np = n / 8;
-  const int64_t want = (np + THREADS - 1) / THREADS;
-  const int64_t cap = (int64_t)device_cu_count() * 32;
-  const unsigned g = (unsigned)(want < cap ? want : cap);
+  const unsigned g = grid_for(np, DEQ_T);
   if (fmt == 0) {
-    if (dtype == 0) k_dequant<0, 0><<<g, THREADS, 0, stream>>>(codes, scales, dst, np);
-    else k_dequant<0, 1><<<g, THREADS, 0, stream>>>(codes, scales, dst, np);
+    if (dtype == 0) k_dequant<0, 0, DEQ_T><<<g, DEQ_T, 0, stream>>>(codes, scales, dst, np);
+    else k_dequant<0, 1, DEQ_T><<<g, DEQ_T, 0, stream>>>(codes, scales, dst, np);
   } else {
-    if (dtype == 0) k_dequant<1, 0><<<g, THREADS, 0, stream>>>(codes, scales, dst, np);
-    else k_dequant<1, 1><<<g, THREADS, 0, stream>>>(codes, scales, dst, np);
+    if (dtype == 0) k_dequant<1, 0, DEQ_T><<<g, DEQ_T, 0, stream>>>(codes, scales, dst, np);
+    else k_dequant<1, 1, DEQ_T><<<g, DEQ_T, 0, stream>>>(codes, scales, dst, np);
   }
   return hipGetLastError();
 }
