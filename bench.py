@@ -68,15 +68,16 @@ def source_hash():
 
 
 def load_traffic(kernel_name):
-    """HBM traffic per launch from the committed counter summary, if it was
-    taken on the current kernel sources."""
+    """HBM bytes per launch (fetched + written) from the committed counter
+    summary, if it was taken on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
     if d.get("source_hash") != source_hash():
         return None
-    return d.get("kernels", {}).get(kernel_name)
+    k = d.get("kernels", {}).get(kernel_name)
+    return None if k is None else k["total_bytes"]
 
 
 def cpu_baseline(x_bits, rots, rows):
@@ -168,6 +169,26 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # dequantize of the codes the step produced (measured beside the step)
+    deq_out = torch.empty_like(x)
+    extras = []
+    for fmt in (0, 1):
+        mx.mx_quantize(fmt, x, codes=codes[fmt], scales=scales)
+        for _ in range(2):
+            mx.mx_dequantize(fmt, codes[fmt], scales, K, dst=deq_out)
+        dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a, b in dev_ev:
+            a.record()
+            mx.mx_dequantize(fmt, codes[fmt], scales, K, dst=deq_out)
+            b.record()
+        torch.cuda.synchronize()
+        avg = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
+        bts = n * ((0.5 if fmt == 0 else 1.0) + 1.0 / 32.0 + 2.0)
+        extras.append({"kernel": f"dequantize_{'mxfp4' if fmt == 0 else 'mxfp8'}_bf16", "bytes": int(bts),
+                       "avg_us": round(avg * 1e3, 2), "GBps": round(bts / (avg * 1e-3) / 1e9, 1),
+                       "frac_of_peak": round(bts / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)})
+    del deq_out
+
     # measured copy ceiling: device-to-device copy of the same layer
     cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
     for a, b in cev:
@@ -224,6 +245,7 @@ def main():
                      "traffic": load_traffic(dom["kernel"])},
         "variants": per,
         "ratios": ratio,
+        "outside_step": extras,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(x_bits, rots, args.cpu_rows)
