@@ -126,6 +126,27 @@ MX_API int mx_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
 MX_API int mx_rotate(const void *src, int src_dtype, int64_t M, int64_t K,
                      const void *rot, int rot_size, float *dst);
 
+/*
+ * MX GEMM: c[M x N] (row-major) = alpha * A_dq . B_dq^T, where A is [M x K]
+ * and B is [N x K], both in the layout mx_quantize writes (codes and
+ * [rows x K/32] scales, K-contiguous: the "TN" operand order), on the CDNA4
+ * scaled matrix cores.  Products of codes are exact, each product carries
+ * the two scales of its groups, and accumulation is fp32; the result is
+ * multiplied by alpha in fp32 and stored as out_dtype (bf16 by
+ * nearest-even rounding, or fp32).  This is the consumer of the quantized
+ * layout, with the call shape and check of the pages' MXFP4 GEMM ("Add
+ * QuTLASS support to vLLM", Purpose: MXFP4 matmul kernel with alpha and
+ * bf16 output; review of the MXFP4 test: compared with a_dq @ b_dq^T).
+ *   codes      16-byte aligned; scales any alignment; c 16-byte aligned.
+ *   K == 0 stores zeros.  M <= 65535 * 128.
+ *   A scale byte of 0xFF (NaN) or an E4M3 NaN code gives NaN in the
+ *   affected outputs.
+ */
+MX_API int mx_matmul(int fmt, const uint8_t *a_codes, const uint8_t *a_scales,
+                     const uint8_t *b_codes, const uint8_t *b_scales,
+                     int64_t M, int64_t N, int64_t K, float alpha,
+                     int out_dtype, void *c);
+
 /* Stream used by the calling thread's subsequent calls (a hipStream_t;
  * NULL = the default stream).  The setting is thread-local. */
 MX_API void mx_set_stream(void *stream);

@@ -6,7 +6,7 @@ entry-point names.  The binding is loaded on first use so that importing
 ``workloads`` does not need the library.
 """
 
-__all__ = ["mx_qdq", "mx_quantize", "mx_dequantize", "mx_rotate",
+__all__ = ["mx_qdq", "mx_quantize", "mx_dequantize", "mx_rotate", "mx_matmul",
            "mx_set_stream", "mx_status_string", "MXError",
            "E2M1", "E4M3", "BF16", "F32"]
 

@@ -34,11 +34,12 @@ _lib.mx_qdq.argtypes = [_int, _vp, _int, _i64, _i64, _vp, _int, _vp]
 _lib.mx_quantize.argtypes = [_int, _vp, _i64, _i64, _vp, _int, _vp, _vp]
 _lib.mx_dequantize.argtypes = [_int, _vp, _vp, _i64, _i64, _int, _vp]
 _lib.mx_rotate.argtypes = [_vp, _int, _i64, _i64, _vp, _int, _vp]
+_lib.mx_matmul.argtypes = [_int, _vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_float, _int, _vp]
 _lib.mx_set_stream.argtypes = [_vp]
 _lib.mx_get_stream.restype = _vp
 _lib.mx_status_string.argtypes = [_int]
 _lib.mx_status_string.restype = ctypes.c_char_p
-for _f in (_lib.mx_qdq, _lib.mx_quantize, _lib.mx_dequantize, _lib.mx_rotate):
+for _f in (_lib.mx_qdq, _lib.mx_quantize, _lib.mx_dequantize, _lib.mx_rotate, _lib.mx_matmul):
     _f.restype = _int
 
 
@@ -143,6 +144,21 @@ def mx_rotate(src: torch.Tensor, rot: torch.Tensor, dst: torch.Tensor | None = N
     _stream()
     _call(_lib.mx_rotate(_dev(src, "src"), _DTYPE[src.dtype], M, K, rp, r, _dev(dst, "dst")))
     return dst
+
+
+def mx_matmul(fmt: int, a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor,
+              b_scales: torch.Tensor, K: int, alpha: float = 1.0, dtype: torch.dtype = torch.bfloat16,
+              c: torch.Tensor | None = None):
+    """[M, N] = alpha * A_dq . B_dq^T from MX codes and scales (A [M, K], B [N, K])."""
+    M, N = a_scales.shape[0], b_scales.shape[0]
+    if c is None:
+        c = torch.empty((M, N), dtype=dtype, device=a_codes.device)
+    if c.dtype not in _DTYPE or tuple(c.shape) != (M, N):
+        raise ValueError("c must be a bfloat16 or float32 [M, N] tensor")
+    _stream()
+    _call(_lib.mx_matmul(fmt, _dev(a_codes, "a_codes"), _dev(a_scales, "a_scales"), _dev(b_codes, "b_codes"),
+                         _dev(b_scales, "b_scales"), M, N, K, float(alpha), _DTYPE[c.dtype], _dev(c, "c")))
+    return c
 
 
 def raw():

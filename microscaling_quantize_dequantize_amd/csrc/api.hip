@@ -111,6 +111,22 @@ MX_API int mx_rotate(const void *src, int src_dtype, int64_t M, int64_t K, const
                                  tl_stream));
 }
 
+MX_API int mx_matmul(int fmt, const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                     const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, float alpha, int out_dtype,
+                     void *c) {
+  int st;
+  if ((st = check_fmt(fmt)) || (st = check_dtype(out_dtype)) || (st = check_shape(M, K)) ||
+      (st = check_shape(N, K)))
+    return st;
+  if (M > ((int64_t)65535 << 7) || (N + 127) / 128 > (int64_t)INT32_MAX) return MX_ESHAPE;  // grid limits
+  if (M == 0 || N == 0) return MX_OK;
+  if (!c) return MX_ENULL;
+  if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return MX_ENULL;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(c, 16)) return MX_EALIGN;
+  return launched(
+      mx::launch_gemm(fmt, a_codes, a_scales, b_codes, b_scales, M, N, K, alpha, out_dtype, c, tl_stream));
+}
+
 MX_API void mx_set_stream(void *stream) { tl_stream = (hipStream_t)stream; }
 
 MX_API void *mx_get_stream(void) { return (void *)tl_stream; }

@@ -22,4 +22,8 @@ hipError_t launch_dequant(int fmt, int dtype, const uint8_t *codes, const uint8_
 hipError_t launch_rot(int fmt, int op, int dtype, const void *src, const void *rot, int r,
                       void *dst, uint8_t *codes, uint8_t *scales, int64_t n, hipStream_t stream);
 
+hipError_t launch_gemm(int fmt, const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs,
+                       int64_t M, int64_t N, int64_t K, float alpha, int out_dtype, void *c,
+                       hipStream_t stream);
+
 }  // namespace mx

@@ -82,6 +82,8 @@ def lib():
         L.orc_quantize.restype = i32
         L.orc_dequantize.argtypes = [i32, vp, vp, i64, i64, i32, vp]
         L.orc_dequantize.restype = i32
+        L.orc_dequantize_f64.argtypes = [i32, vp, vp, i64, i64, vp]
+        L.orc_dequantize_f64.restype = i32
         _lib = L
     return _lib
 
@@ -252,3 +254,31 @@ def dequantize(fmt: int, codes: np.ndarray, scales: np.ndarray, K: int,
 
     _run_rows(run, M, threads)
     return dst
+
+
+def dequantize_f64(fmt: int, codes: np.ndarray, scales: np.ndarray, K: int, threads: int = 1):
+    """Exact dequantized values (float64 [M, K]), not rounded to a storage type."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    M = scales.shape[0]
+    dst = np.empty((M, K), dtype=np.float64)
+
+    def run(r0, r1):
+        rc = lib().orc_dequantize_f64(fmt, codes[r0:].ctypes.data, scales[r0:].ctypes.data,
+                                      r1 - r0, K, dst[r0:].ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+
+    _run_rows(run, M, threads)
+    return dst
+
+
+def matmul(fmt: int, a_codes, a_scales, b_codes, b_scales, K: int, threads: int = 1):
+    """MX GEMM reference: float64 A_dq . B_dq^T for A [M, K] and B [N, K] in the
+    quantized layout ("Add QuTLASS support to vLLM", review of the MXFP4 test:
+    the kernel's output is compared with the dequantized operands multiplied in
+    high precision).  The two exact dequantizations are followed by one library
+    matmul in float64."""
+    a = dequantize_f64(fmt, a_codes, a_scales, K, threads)
+    b = dequantize_f64(fmt, b_codes, b_scales, K, threads)
+    return a @ b.T

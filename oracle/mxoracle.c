@@ -424,3 +424,24 @@ int orc_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
     }
     return 0;
 }
+
+int orc_dequantize_f64(int fmt, const uint8_t *codes, const uint8_t *scales,
+                       int64_t M, int64_t K, double *dst)
+{
+    if (!valid_fmt(fmt) || !valid_shape(M, K, 0, NULL))
+        return -1;
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t col = 0; col < K; ++col) {
+            int64_t idx = i * K + col;
+            int b = scales[idx / 32];
+            int code;
+            if (fmt == ORC_E4M3)
+                code = codes[idx];
+            else
+                code = (col % 2 == 0) ? (codes[idx / 2] & 0xF)
+                                      : (codes[idx / 2] >> 4);
+            dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 127);
+        }
+    }
+    return 0;
+}

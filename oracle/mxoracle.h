@@ -104,6 +104,14 @@ int orc_quantize(int fmt, const void *src, int64_t M, int64_t K,
 int orc_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
                    int64_t M, int64_t K, int dst_dtype, void *dst);
 
+/* The same dequantized values kept in double, with no rounding into a
+ * storage type: the exact operands of an MX GEMM (the MXFP4 GEMM test on
+ * "Add QuTLASS support to vLLM" multiplies dequantized operands in high
+ * precision).  Every MX value (at most 8 significant bits times a power of
+ * two in [2^-127, 2^127]) is exact in double. */
+int orc_dequantize_f64(int fmt, const uint8_t *codes, const uint8_t *scales,
+                       int64_t M, int64_t K, double *dst);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,7 @@ def lib():
     L.mx_quantize.argtypes = [i, vp, i64, i64, vp, i, vp, vp]
     L.mx_dequantize.argtypes = [i, vp, vp, i64, i64, i, vp]
     L.mx_rotate.argtypes = [vp, i, i64, i64, vp, i, vp]
+    L.mx_matmul.argtypes = [i, vp, vp, vp, vp, i64, i64, i64, ctypes.c_float, i, vp]
     L.mx_set_stream.argtypes = [vp]
     L.mx_get_stream.restype = vp
     L.mx_status_string.argtypes = [i]
@@ -38,7 +39,7 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     names = set(declared_symbols())
-    assert {"mx_qdq", "mx_quantize", "mx_dequantize", "mx_rotate", "mx_set_stream",
+    assert {"mx_qdq", "mx_quantize", "mx_dequantize", "mx_rotate", "mx_matmul", "mx_set_stream",
             "mx_get_stream", "mx_status_string"} <= names
 
 
@@ -102,6 +103,21 @@ def test_dequantize_and_rotate_argument_errors(lib):
     assert lib.mx_rotate(A, 0, 4, 64, A, 16, None) == MX_ENULL
 
 
+def test_matmul_argument_errors(lib):
+    assert lib.mx_matmul(2, A, A, A, A, 4, 4, 64, 1.0, 0, A) == MX_EFMT
+    assert lib.mx_matmul(0, A, A, A, A, 4, 4, 64, 1.0, 5, A) == MX_EDTYPE
+    assert lib.mx_matmul(0, A, A, A, A, 4, 4, 48, 1.0, 0, A) == MX_ESHAPE
+    assert lib.mx_matmul(0, A, A, A, A, -1, 4, 64, 1.0, 0, A) == MX_ESHAPE
+    assert lib.mx_matmul(0, A, A, A, A, 4, -4, 64, 1.0, 0, A) == MX_ESHAPE
+    assert lib.mx_matmul(1, A, A, A, A, 65535 * 128 + 1, 4, 64, 1.0, 1, A) == MX_ESHAPE
+    assert lib.mx_matmul(0, A, A, A, A, 4, 4, 64, 1.0, 0, None) == MX_ENULL
+    assert lib.mx_matmul(0, A, None, A, A, 4, 4, 64, 1.0, 0, A) == MX_ENULL
+    assert lib.mx_matmul(0, A, A, None, A, 4, 4, 64, 1.0, 0, A) == MX_ENULL
+    assert lib.mx_matmul(0, A + 4, A, A, A, 4, 4, 64, 1.0, 0, A) == MX_EALIGN
+    assert lib.mx_matmul(0, A, A, A + 8, A, 4, 4, 64, 1.0, 0, A) == MX_EALIGN
+    assert lib.mx_matmul(0, A, A, A, A, 4, 4, 64, 1.0, 1, A + 4) == MX_EALIGN
+
+
 def test_empty_is_a_noop(lib):
     # no pointer is touched and no kernel is launched for M == 0 or K == 0
     assert lib.mx_qdq(0, None, 0, 0, 64, None, 0, None) == MX_OK
@@ -109,6 +125,8 @@ def test_empty_is_a_noop(lib):
     assert lib.mx_quantize(0, None, 0, 128, None, 0, None, None) == MX_OK
     assert lib.mx_dequantize(1, None, None, 0, 32, 0, None) == MX_OK
     assert lib.mx_rotate(None, 0, 0, 128, A, 128, None) == MX_OK
+    assert lib.mx_matmul(0, None, None, None, None, 0, 8, 64, 1.0, 0, None) == MX_OK
+    assert lib.mx_matmul(1, None, None, None, None, 8, 0, 64, 1.0, 1, None) == MX_OK
 
 
 def test_status_strings_and_stream(lib):

@@ -1,0 +1,233 @@
+"""GPU parity of the MX GEMM consumer (mx_matmul) against the CPU oracle's
+float64 A_dq . B_dq^T, through the C ABI (thin binding).
+
+The pages check their MXFP4 GEMM the same way: the kernel's output against
+the dequantized operands multiplied in high precision ("Add QuTLASS support to
+vLLM", review of the MXFP4 test).  Two bars:
+  * exact: codes and scales drawn from a narrow range in which every partial
+    sum is a multiple of a power of two small enough for fp32 to hold exactly,
+    so fp32 accumulation in any order gives the exact result and the output
+    must match bit for bit (fp32, or its single nearest-even bf16 rounding);
+  * realistic: operands quantized by the oracle from N(0,1)-like data; the
+    error of fp32 accumulation over K terms in any order is at most
+    K * 2^-24 * sum_k |a_k b_k| (plus one rounding of the alpha product and,
+    for bf16 output, one bf16 rounding).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from _parity import E2M1, E4M3, THREADS, assert_bits_equal, bits_of, to_gpu_bf16
+from microscaling_quantize_dequantize_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from microscaling_quantize_dequantize_amd import binding
+    return binding
+
+
+def gpu_u8(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def code_bytes(fmt, K):
+    return K // 2 if fmt == E2M1 else K
+
+
+def narrow_operand(fmt, rows, K, rng):
+    """Codes and scales (2^-1..2^1) whose dequantized values are multiples of
+    2^-2 (E2M1) or 2^-5 (E4M3) with |v| <= 12 (E2M1) or 7.5 (E4M3)."""
+    if fmt == E2M1:
+        codes = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)  # every E2M1 code
+    else:
+        e = rng.integers(6, 9, (rows, K))  # exponent field 6..8: |v| in [0.5, 3.75]
+        m = rng.integers(0, 8, (rows, K))
+        sign = rng.integers(0, 2, (rows, K)) << 7
+        codes = (sign | (e << 3) | m).astype(np.uint8)
+        codes[rng.random((rows, K)) < 0.1] = 0
+    scales = rng.integers(126, 129, (rows, K // 32), dtype=np.uint8)
+    return codes, scales
+
+
+def run(mx, fmt, ac, as_, bc, bs, K, alpha=1.0, dtype=None):
+    import torch
+    dtype = dtype or torch.float32
+    c = mx.mx_matmul(fmt, gpu_u8(ac), gpu_u8(as_), gpu_u8(bc), gpu_u8(bs), K, alpha=alpha, dtype=dtype)
+    torch.cuda.synchronize()
+    return c
+
+
+def values(t) -> np.ndarray:
+    import torch
+    return t.detach().float().cpu().numpy().astype(np.float64) if t.dtype == torch.bfloat16 \
+        else t.detach().cpu().numpy().astype(np.float64)
+
+
+# K kept where every |partial sum| stays below 2^24 times the product grid step
+EXACT_SHAPES = [(1, 1, 32), (128, 128, 128), (200, 136, 160), (33, 257, 96), (256, 384, 256), (130, 70, 512)]
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+@pytest.mark.parametrize("shape", EXACT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_exact_small_range(mx, fmt, shape):
+    import torch
+    M, N, K = shape
+    if fmt == E4M3 and K > 256:
+        K = 256  # E4M3 products reach 56.25 on a 2^-10 grid: sum of |p| < 2^14 needs K <= 291
+    rng = np.random.default_rng([fmt, M, N, K])
+    ac, as_ = narrow_operand(fmt, M, K, rng)
+    bc, bs = narrow_operand(fmt, N, K, rng)
+    ref = oracle.matmul(fmt, ac, as_, bc, bs, K)
+    # the premise of the exact bar: the exact result is an fp32 value
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
+    got = run(mx, fmt, ac, as_, bc, bs, K)
+    assert_bits_equal(bits_of(got), ref.astype(np.float32).view(np.uint32), f"fp32 gemm fmt{fmt} {shape}")
+    # alpha a power of two keeps the result exact; bf16 output is its one rounding
+    got = run(mx, fmt, ac, as_, bc, bs, K, alpha=0.25, dtype=torch.bfloat16)
+    want = W.f32_to_bf16_bits((ref * 0.25).astype(np.float32))
+    assert_bits_equal(bits_of(got), want, f"bf16 gemm fmt{fmt} {shape}")
+
+
+def check_within_bound(got, ref, absprod, K, alpha, bf16):
+    bound = (K * U * absprod + U * np.abs(ref)) * abs(alpha)
+    if bf16:
+        bound = bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(alpha * ref)
+    err = np.abs(got - alpha * ref)
+    bad = err > bound
+    assert not bad.any(), (f"{int(bad.sum())} outputs outside the fp32-accumulation bound; "
+                           f"worst excess {float((err - bound).max()):.3e}")
+
+
+def quantized_operand(fmt, rows, K, seed, spread):
+    """Oracle-quantized N(0,1) bf16 rows with per-row magnitudes 2^[-spread, spread]."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, K)) * np.exp2(rng.integers(-spread, spread + 1, (rows, 1)))
+    bits = W.f32_to_bf16_bits(x.astype(np.float32))
+    return oracle.quantize(fmt, bits, threads=THREADS)
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+@pytest.mark.parametrize("shape", [(256, 320, 1024), (77, 45, 224), (129, 257, 2080)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_quantized_operands_within_bound(mx, fmt, shape):
+    import torch
+    M, N, K = shape
+    ac, as_ = quantized_operand(fmt, M, K, 100 + fmt, 6)
+    bc, bs = quantized_operand(fmt, N, K, 200 + fmt, 3)
+    ref = oracle.matmul(fmt, ac, as_, bc, bs, K)
+    a = oracle.dequantize_f64(fmt, ac, as_, K)
+    b = oracle.dequantize_f64(fmt, bc, bs, K)
+    absprod = np.abs(a) @ np.abs(b).T
+    for alpha, dtype in ((1.0, torch.float32), (0.37, torch.float32), (1.5, torch.bfloat16)):
+        got = values(run(mx, fmt, ac, as_, bc, bs, K, alpha=alpha, dtype=dtype))
+        check_within_bound(got, ref, absprod, K, alpha, dtype == torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_quantize_then_matmul_chain(mx, fmt):
+    """The pages' chain: quantize activations and weights on the GPU, then feed
+    the codes and scales straight into the GEMM.  The GPU codes must equal the
+    oracle's, and the product must be within the bound of the oracle's."""
+    import torch
+    M, N, K = 192, 160, 512
+    xa = W.random_bf16((M, K), seed=31)
+    xb = W.random_bf16((N, K), seed=32, scale=0.02)
+    ga, gsa = mx.mx_quantize(fmt, to_gpu_bf16(xa))
+    gb, gsb = mx.mx_quantize(fmt, to_gpu_bf16(xb))
+    oa, osa = oracle.quantize(fmt, xa, threads=THREADS)
+    ob, osb = oracle.quantize(fmt, xb, threads=THREADS)
+    torch.cuda.synchronize()
+    for g, o, what in ((ga, oa, "a codes"), (gsa, osa, "a scales"), (gb, ob, "b codes"), (gsb, osb, "b scales")):
+        assert_bits_equal(bits_of(g), o, what)
+    c = mx.mx_matmul(fmt, ga, gsa, gb, gsb, K, dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.matmul(fmt, oa, osa, ob, osb, K)
+    absprod = np.abs(oracle.dequantize_f64(fmt, oa, osa, K)) @ np.abs(oracle.dequantize_f64(fmt, ob, osb, K)).T
+    check_within_bound(values(c), ref, absprod, K, 1.0, False)
+
+
+def test_k_zero_writes_zeros(mx):
+    import torch
+    for dtype in (torch.float32, torch.bfloat16):
+        c = torch.full((5, 7), float("nan"), dtype=dtype, device="cuda")
+        e = torch.empty(0, dtype=torch.uint8, device="cuda")
+        s = torch.empty((5, 0), dtype=torch.uint8, device="cuda")
+        t = torch.empty((7, 0), dtype=torch.uint8, device="cuda")
+        mx.mx_matmul(E2M1, e, s, e, t, 0, c=c)
+        torch.cuda.synchronize()
+        assert (c == 0).all()
+
+
+def test_empty_and_bad_arguments(mx):
+    import torch
+    e = torch.empty((0, 16), dtype=torch.uint8, device="cuda")
+    s = torch.empty((0, 1), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((4, 16), dtype=torch.uint8, device="cuda")
+    bs = torch.full((4, 1), 127, dtype=torch.uint8, device="cuda")
+    assert mx.mx_matmul(E2M1, e, s, b, bs, 32).shape == (0, 4)
+    with pytest.raises(mx.MXError):
+        mx.mx_matmul(E2M1, b, bs, b, bs, 48)  # K not a multiple of 32
+    with pytest.raises(ValueError):
+        mx.mx_matmul(E2M1, b, bs, b, bs, 32, c=torch.empty((4, 5), device="cuda"))
+
+
+def test_nan_scale_and_nan_code_propagate(mx):
+    import torch
+    K = 64
+    rng = np.random.default_rng(9)
+    ac, as_ = narrow_operand(E4M3, 4, K, rng)
+    bc, bs = narrow_operand(E4M3, 3, K, rng)
+    as_[1, 1] = 0xFF  # NaN scale: row 1 of A
+    bc[2, 5] = 0x7F   # NaN code: row 2 of B
+    got = values(run(mx, E4M3, ac, as_, bc, bs, K))
+    ref = oracle.matmul(E4M3, ac, as_, bc, bs, K)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.isnan(ref[1]).all() and np.isnan(ref[:, 2]).all()
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+# ---- the GEMM shape timed beside the step: down-projection consumer --------
+# A: [8192 x 28672] activations, B: [8192 x 28672] weights, C: [8192 x 8192]
+
+FULL_M, FULL_N, FULL_K = 8192, 8192, 28672
+
+
+def full_operand(fmt, rows, seed):
+    rng = np.random.default_rng(seed)
+    cb = code_bytes(fmt, FULL_K)
+    codes = rng.integers(0, 256, (rows, cb), dtype=np.uint8)
+    if fmt == E4M3:
+        codes[(codes & 0x7F) == 0x7F] ^= 0x01  # keep NaN codes out
+    scales = rng.integers(118, 126, (rows, FULL_K // 32), dtype=np.uint8)
+    return codes, scales
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_full_size_sampled(mx, fmt):
+    import torch
+    ac, as_ = full_operand(fmt, FULL_M, 700 + fmt)
+    bc, bs = full_operand(fmt, FULL_N, 800 + fmt)
+    c = run(mx, fmt, ac, as_, bc, bs, FULL_K, dtype=torch.bfloat16)
+    rng = np.random.default_rng(fmt)
+    # sampled rows and columns, including both ends of each dimension and a 128-tile seam
+    rows = np.unique(np.concatenate([[0, 127, 128, FULL_M - 1], rng.integers(0, FULL_M, 60)]))
+    cols = np.unique(np.concatenate([[0, 127, 128, FULL_N - 1], rng.integers(0, FULL_N, 60)]))
+    a = oracle.dequantize_f64(fmt, ac[rows], as_[rows], FULL_K, threads=THREADS)
+    b = oracle.dequantize_f64(fmt, bc[cols], bs[cols], FULL_K, threads=THREADS)
+    ref = a @ b.T
+    absprod = np.abs(a) @ np.abs(b).T
+    cv = values(c)
+    check_within_bound(cv[np.ix_(rows, cols)], ref, absprod, FULL_K, 1.0, True)
+    assert math.isfinite(float(cv.sum()))

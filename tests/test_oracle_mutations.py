@@ -21,6 +21,10 @@ MUTANTS = {
     "no_subnormal_grid": ("if (e < f->emin)\n        e = f->emin;\n    double ulp", "double ulp"),
     "bf16_subnormal_exponent": ("ldexp((double)man, -133)", "ldexp((double)man, -134)"),
     "scale_from_first_element": ("else if (fabs(y[j]) > amax)", "else if (j == 0)"),
+    "exact_dequant_scale_bias": ("dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 127);",
+                                 "dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 128);"),
+    "exact_dequant_sign_dropped": ("dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 127);",
+                                   "dst[idx] = (b == 0xFF) ? NAN : ldexp(fabs(orc_decode(fmt, code)), b - 127);"),
 }
 
 

@@ -426,3 +426,89 @@ def test_rejects_bad_arguments(orc):
     x = W.random_bf16((2, 64), seed=1)
     with pytest.raises(ValueError):
         orc.qdq(E2M1, x, W.hadamard_rotation(128), 128)  # K % r != 0
+
+
+# ---- the MX GEMM reference ---------------------------------------------------
+
+def textbook_value(fmt, code):
+    """Signed value of one element code from the format definitions."""
+    sign = -1.0 if code & SIGN_BIT[fmt] else 1.0
+    mag = code & (SIGN_BIT[fmt] - 1)
+    if fmt == E4M3 and mag == 0x7F:
+        return math.nan
+    return sign * float(textbook_grid(fmt)[mag])
+
+
+def textbook_row(fmt, code_row, scale_row, K):
+    """One dequantized row by plain Python loops (E2M1: even column in the low
+    nibble)."""
+    out = []
+    for k in range(K):
+        if fmt == E2M1:
+            byte = int(code_row[k // 2])
+            code = byte & 0xF if k % 2 == 0 else byte >> 4
+        else:
+            code = int(code_row[k])
+        out.append(textbook_value(fmt, code) * 2.0 ** (int(scale_row[k // 32]) - 127))
+    return out
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_matmul_brute_force(orc, fmt):
+    rng = np.random.default_rng(11 + fmt)
+    M, N, K = 3, 4, 96
+    cb = K // 2 if fmt == E2M1 else K
+    ac = rng.integers(0, 256, (M, cb), dtype=np.uint8)
+    bc = rng.integers(0, 256, (N, cb), dtype=np.uint8)
+    if fmt == E4M3:  # keep NaN codes out of the sum
+        ac[(ac & 0x7F) == 0x7F] = 0x12
+        bc[(bc & 0x7F) == 0x7F] = 0x34
+    as_ = rng.integers(120, 135, (M, K // 32), dtype=np.uint8)
+    bs = rng.integers(120, 135, (N, K // 32), dtype=np.uint8)
+    got = orc.matmul(fmt, ac, as_, bc, bs, K)
+    arow = [textbook_row(fmt, ac[i], as_[i], K) for i in range(M)]
+    brow = [textbook_row(fmt, bc[j], bs[j], K) for j in range(N)]
+    for i in range(M):
+        for j in range(N):
+            want = math.fsum(x * y for x, y in zip(arow[i], brow[j]))
+            assert got[i, j] == pytest.approx(want, rel=1e-14, abs=1e-300)
+
+
+def test_matmul_constant_groups_closed_form(orc):
+    # every E2M1 element 1.0 (code 0x2); per-group scales: the dot product
+    # is 32 * sum_g 2^(sa_g + sb_g - 254)
+    K = 128
+    a = np.full((2, K // 2), 0x22, np.uint8)
+    b = np.full((3, K // 2), 0x22, np.uint8)
+    as_ = np.array([[127, 128, 126, 130], [100, 127, 127, 127]], np.uint8)
+    bs = np.array([[127, 127, 127, 127], [131, 120, 127, 128], [127, 126, 129, 127]], np.uint8)
+    got = orc.matmul(E2M1, a, as_, b, bs, K)
+    for i in range(2):
+        for j in range(3):
+            want = 32 * sum(2.0 ** (int(as_[i, g]) + int(bs[j, g]) - 254) for g in range(4))
+            assert got[i, j] == want
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_matmul_one_hot_rows_pick_columns_of_b(orc, fmt):
+    # A row i is 1.0 at column k_i and 0 elsewhere, so C[i, j] = B_dq[j, k_i]:
+    # pins the orientation (A . B^T, not A^T . B) and the nibble order
+    K, N = 64, 5
+    ks = [0, 1, 30, 33, 63]
+    one = 0x2 if fmt == E2M1 else 0x38  # 1.0 in E2M1 / E4M3
+    a = np.zeros((len(ks), K // 2 if fmt == E2M1 else K), np.uint8)
+    for i, k in enumerate(ks):
+        if fmt == E2M1:
+            a[i, k // 2] = one if k % 2 == 0 else one << 4
+        else:
+            a[i, k] = one
+    as_ = np.full((len(ks), K // 32), 127, np.uint8)
+    rng = np.random.default_rng(5)
+    b = rng.integers(0, 256, (N, a.shape[1]), dtype=np.uint8)
+    if fmt == E4M3:
+        b[(b & 0x7F) == 0x7F] = 0
+    bs = rng.integers(124, 131, (N, K // 32), dtype=np.uint8)
+    got = orc.matmul(fmt, a, as_, b, bs, K)
+    for i, k in enumerate(ks):
+        for j in range(N):
+            assert got[i, j] == textbook_row(fmt, b[j], bs[j], K)[k]
