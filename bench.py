@@ -59,10 +59,13 @@ def name_of(op, fmt, r):
     return f"{op}_{'mxfp4' if fmt == 0 else 'mxfp8'}_rot{r}"
 
 
+STEP_SOURCES = ("unrot.hip", "rot.hip", "mx_device.h")  # what the step's kernels are built from
+
+
 def source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "microscaling_quantize_dequantize_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in STEP_SOURCES:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -80,26 +83,64 @@ def load_traffic(kernel_name):
     return None if k is None else k["total_bytes"]
 
 
-def cpu_baseline(x_bits, rots, rows):
+def cpu_baseline(x_bits, rots, rows, rows_1t):
     import numpy as np
 
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
+
+    def run(sample, t):
+        total = 0.0
+        t0 = time.perf_counter()
+        for op, fmt, r in variants():
+            R = rots[r][0] if r else None
+            if op == "qdq":
+                oracle.qdq(fmt, sample, R, r, threads=t)
+            else:
+                oracle.quantize(fmt, sample, R, r, threads=t)
+            total += sample.size * bytes_per_element(op, fmt)
+        return total, time.perf_counter() - t0
+
     sample = np.ascontiguousarray(x_bits[:rows])
-    n = sample.size
-    total_bytes = 0.0
-    t0 = time.perf_counter()
-    for op, fmt, r in variants():
-        R = rots[r][0] if r else None
-        if op == "qdq":
-            oracle.qdq(fmt, sample, R, r, threads=threads)
-        else:
-            oracle.quantize(fmt, sample, R, r, threads=threads)
-        total_bytes += n * bytes_per_element(op, fmt)
-    dt = time.perf_counter() - t0
+    total_bytes, dt = run(sample, threads)
+    b1, dt1 = run(np.ascontiguousarray(x_bits[:rows_1t]), 1)
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0-{rows - 1} of the 8192x57344 layer ({n} elements), all 12 step variants, "
-                      f"{dt:.1f} s wall", "seconds": round(dt, 2)}
+            "sample": f"rows 0-{rows - 1} of the 8192x57344 layer ({sample.size} elements), all 12 step "
+                      f"variants, {dt:.1f} s wall on {threads} threads; single thread: rows 0-{rows_1t - 1}, "
+                      f"{dt1:.1f} s", "seconds": round(dt, 2),
+            "single_thread_value": round(b1 / dt1 / 1e9, 5),
+            "host": host_cpu()}
+
+
+def host_cpu():
+    model, smt = None, None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+        smt = open("/sys/devices/system/cpu/smt/active").read().strip() == "1"
+    except OSError:
+        pass
+    return {"model": model, "nproc": os.cpu_count(), "smt": smt}
+
+
+def timed(fn, reps):
+    """Average and minimum duration (ms) of fn() over reps launches, each
+    bracketed by events on torch's current stream."""
+    import numpy as np
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return float(np.mean(ms)), float(np.min(ms))
+
+
+GEMM_PEAK_TFLOPS = {0: 10100.0, 1: 5000.0}  # MI355X dense fp4 / fp8 matrix peaks
 
 
 def main():
@@ -109,6 +150,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-rows-1t", type=int, default=64)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -169,25 +211,48 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # dequantize of the codes the step produced (measured beside the step)
+    # beside the step: dequantize of the step's codes, the transposed layout
+    # of the layer, and the GEMM that consumes quantized operands
     deq_out = torch.empty_like(x)
     extras = []
     for fmt in (0, 1):
         mx.mx_quantize(fmt, x, codes=codes[fmt], scales=scales)
         for _ in range(2):
             mx.mx_dequantize(fmt, codes[fmt], scales, K, dst=deq_out)
-        dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-        for a, b in dev_ev:
-            a.record()
-            mx.mx_dequantize(fmt, codes[fmt], scales, K, dst=deq_out)
-            b.record()
-        torch.cuda.synchronize()
-        avg = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
+        avg, mn = timed(lambda: mx.mx_dequantize(fmt, codes[fmt], scales, K, dst=deq_out), 10)
         bts = n * ((0.5 if fmt == 0 else 1.0) + 1.0 / 32.0 + 2.0)
         extras.append({"kernel": f"dequantize_{'mxfp4' if fmt == 0 else 'mxfp8'}_bf16", "bytes": int(bts),
-                       "avg_us": round(avg * 1e3, 2), "GBps": round(bts / (avg * 1e-3) / 1e9, 1),
+                       "avg_us": round(avg * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                       "GBps": round(bts / (avg * 1e-3) / 1e9, 1),
                        "frac_of_peak": round(bts / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)})
+    xt, dt_ = x.view(K, M), deq_out.view(K, M)  # the same bytes read as 57344 x 8192
+    for fmt in (0, 1):
+        mx.mx_qdq(fmt, xt, dst=dt_)
+        avg, mn = timed(lambda: mx.mx_qdq(fmt, xt, dst=dt_), 10)
+        extras.append({"kernel": f"qdq_{'mxfp4' if fmt == 0 else 'mxfp8'}_rot0_layout{K}x{M}", "bytes": 4 * n,
+                       "avg_us": round(avg * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                       "GBps": round(4 * n / (avg * 1e-3) / 1e9, 1),
+                       "frac_of_peak": round(4 * n / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)})
     del deq_out
+    # GEMM consumer: the layer's bytes read as two [8192 x 28672] operands
+    # (activations and weights of a down projection), quantized, then
+    # C[8192 x 8192] (bf16) = A_dq . B_dq^T on the scaled matrix cores
+    gm, gk = 8192, n // (2 * 8192)
+    gx = x.view(2 * gm, gk)
+    gc = torch.empty((gm, gm), dtype=torch.bfloat16, device=dev)
+    for fmt in (0, 1):
+        cq, sq = mx.mx_quantize(fmt, gx)
+        a, b_, sa, sb = cq[:gm], cq[gm:], sq[:gm], sq[gm:]
+        for _ in range(2):
+            mx.mx_matmul(fmt, a, sa, b_, sb, gk, c=gc)
+        avg, mn = timed(lambda: mx.mx_matmul(fmt, a, sa, b_, sb, gk, c=gc), 10)
+        tflops = 2.0 * gm * gm * gk / (avg * 1e-3) / 1e12
+        extras.append({"kernel": f"matmul_{'mxfp4' if fmt == 0 else 'mxfp8'}_{gm}x{gm}x{gk}_bf16out",
+                       "flops": 2 * gm * gm * gk, "avg_us": round(avg * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                       "TFLOPs": round(tflops, 1), "bound": "mfma", "peak_TFLOPs": GEMM_PEAK_TFLOPS[fmt],
+                       "frac_of_peak": round(tflops / GEMM_PEAK_TFLOPS[fmt], 4)})
+        del cq, sq, a, b_, sa, sb
+    del gc
 
     # measured copy ceiling: device-to-device copy of the same layer
     cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
@@ -207,7 +272,7 @@ def main():
         b = n * bytes_per_element(op, fmt)
         step_bytes += b
         per.append({"kernel": name_of(op, fmt, r), "bytes": int(b), "avg_us": round(avg * 1e3, 2),
-                    "min_us": round(min(ms) * 1e3, 2), "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+                    "median_us": round(float(np.median(ms)) * 1e3, 2), "min_us": round(min(ms) * 1e3, 2), "GBps": round(b / (avg * 1e-3) / 1e9, 1),
                     "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4),
                     "frac_of_copy": round(b / (avg * 1e-3) / 1e9 / copy_gbps, 4),
                     "elements_per_s": round(n / (avg * 1e-3), 1)})
@@ -248,7 +313,7 @@ def main():
         "outside_step": extras,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(x_bits, rots, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(x_bits, rots, args.cpu_rows, args.cpu_rows_1t)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

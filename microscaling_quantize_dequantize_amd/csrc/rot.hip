@@ -162,6 +162,27 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
   __shared__ u32x4 sA[NJT * NKB * 64];
   __shared__ u32x4 sT[WAVES][TP];
 
+  // R (r*r <= RB*RB bf16) is first copied into the tile buffers with
+  // coalesced 16-byte loads, all in flight at once; the fragments are then
+  // gathered from LDS.
+  static_assert(sizeof(sT) >= RB * RB * 2, "R is staged in the tile buffers");
+  {
+    constexpr int RP = (RB * RB / 8 + THREADS - 1) / THREADS;  // 16-byte pieces per thread
+    const int pieces = r * r / 8;
+    u32x4 rv[RP];
+#pragma unroll
+    for (int k = 0; k < RP; ++k) {
+      const int i = threadIdx.x + k * THREADS;
+      if (i < pieces) rv[k] = ((const u32x4 *)rot)[i];
+    }
+#pragma unroll
+    for (int k = 0; k < RP; ++k) {
+      const int i = threadIdx.x + k * THREADS;
+      if (i < pieces) (&sT[0][0])[i] = rv[k];
+    }
+  }
+  __syncthreads();
+  const uint16_t *Rs = (const uint16_t *)&sT[0][0];
   // A fragment (jt, kb) of lane ln: Reff[t][j] for j = 32*jt + ln%32 and
   // t = 16*kb + 8*(ln/32) + i, i = 0..7.
   for (int idx = threadIdx.x; idx < NJT * NKB * 64; idx += THREADS) {
@@ -170,7 +191,7 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
     unsigned w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = (unsigned)reff(rot, r, t0 + 2 * i, j) | ((unsigned)reff(rot, r, t0 + 2 * i + 1, j) << 16);
+      w[i] = (unsigned)reff(Rs, r, t0 + 2 * i, j) | ((unsigned)reff(Rs, r, t0 + 2 * i + 1, j) << 16);
     sA[idx] = u32x4{w[0], w[1], w[2], w[3]};
   }
   __syncthreads();
@@ -401,10 +422,13 @@ __global__ __launch_bounds__(DTHREADS) void k_rot_f32(const float *__restrict__ 
 // Launch shape of the staged kernels: workgroup size and workgroups per CU
 // in the grid.  LDS per workgroup is RB*RB*2 bytes of A fragments plus a
 // 64*RB-byte tile buffer per wave.  Chosen by measurement on MI355X (8192 x
-// 57344 bf16, QDQ and quantize); the persistent grid amortises the A staging.
+// 57344 bf16, QDQ and quantize).  For RB = 128 only two workgroups fit in a
+// CU's LDS, and a grid of exactly that many (persistent) is fastest: a grid
+// that is not a multiple of the resident count leaves a partial last round.
+// For RB = 64 a grid of 32 per CU (about 3.5 tiles per wave) is fastest.
 template <int RB> struct StagedCfg;
 template <> struct StagedCfg<32> { static constexpr int threads = 1024, per_cu = 8; };
-template <> struct StagedCfg<64> { static constexpr int threads = 512, per_cu = 8; };
+template <> struct StagedCfg<64> { static constexpr int threads = 512, per_cu = 32; };
 template <> struct StagedCfg<128> { static constexpr int threads = 256, per_cu = 2; };
 
 static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
