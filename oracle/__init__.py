@@ -84,6 +84,10 @@ def lib():
         L.orc_dequantize.restype = i32
         L.orc_dequantize_f64.argtypes = [i32, vp, vp, i64, i64, vp]
         L.orc_dequantize_f64.restype = i32
+        L.orc_blocked_size.argtypes = [i64, i64]
+        L.orc_blocked_size.restype = i64
+        L.orc_scales_to_blocked.argtypes = [vp, i64, i64, vp]
+        L.orc_scales_to_blocked.restype = i32
         _lib = L
     return _lib
 
@@ -282,3 +286,17 @@ def matmul(fmt: int, a_codes, a_scales, b_codes, b_scales, K: int, threads: int 
     a = dequantize_f64(fmt, a_codes, a_scales, K, threads)
     b = dequantize_f64(fmt, b_codes, b_scales, K, threads)
     return a @ b.T
+
+
+def blocked_size(M: int, K: int) -> int:
+    return int(lib().orc_blocked_size(M, K))
+
+
+def scales_to_blocked(scales: np.ndarray, K: int) -> np.ndarray:
+    """Row-major [M, K/32] E8M0 scales -> the blocked layout (uint8, flat)."""
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    M = scales.shape[0]
+    out = np.empty(blocked_size(M, K), dtype=np.uint8)
+    if lib().orc_scales_to_blocked(scales.ctypes.data, M, K, out.ctypes.data) != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out

@@ -445,3 +445,33 @@ int orc_dequantize_f64(int fmt, const uint8_t *codes, const uint8_t *scales,
     }
     return 0;
 }
+
+int64_t orc_blocked_size(int64_t M, int64_t K)
+{
+    if (M < 0 || K < 0 || K % 32 != 0)
+        return -1;
+    int64_t row_blocks = (M + 31) / 32;
+    int64_t group_blocks = (K / 32 + 7) / 8;
+    return row_blocks * group_blocks * 256;
+}
+
+int orc_scales_to_blocked(const uint8_t *scales, int64_t M, int64_t K,
+                          uint8_t *out)
+{
+    int64_t size = orc_blocked_size(M, K);
+    if (size < 0)
+        return -1;
+    int64_t G = K / 32;
+    int64_t group_blocks = (G + 7) / 8;
+    for (int64_t b = 0; b < size; ++b)
+        out[b] = 127; /* padding: the scale 2^0 */
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t g = 0; g < G; ++g) {
+            int64_t block = (i / 32) * group_blocks + g / 8;
+            int64_t lane = 32 * (g % 2) + i % 32;
+            int64_t byte = (g % 8) / 2;
+            out[block * 256 + 4 * lane + byte] = scales[i * G + g];
+        }
+    }
+    return 0;
+}

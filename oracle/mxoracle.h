@@ -112,6 +112,25 @@ int orc_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
 int orc_dequantize_f64(int fmt, const uint8_t *codes, const uint8_t *scales,
                        int64_t M, int64_t K, double *dst);
 
+/* Blocked scale layout (a reading: the pages name a padded, blocked scale
+ * tensor -- "Add QuTLASS support to vLLM", review of vllm/_custom_ops.py
+ * and vllm/qutlass_utils/utils.py: padded_rows x padded_cols, to_blocked;
+ * FlashInfer cute-dsl digest page: is_sf_swizzled_layout -- but define it
+ * only for another GPU's matrix cores).  Here the blocks are the operand
+ * order of the gfx950 scaled MFMA with 32x32 tiles and 64-deep k-steps:
+ *   rows are padded to a multiple of 32 and the K/32 groups of a row to a
+ *   multiple of 8; the scales form 256-byte blocks of 32 rows x 8 groups,
+ *   blocks in row-major order over (row block, group block);
+ *   in a block, the 32-bit word l (l = 0..63) holds, for row l%32 of the
+ *   block and h = l/32, the scales of groups h, 2+h, 4+h and 6+h of the
+ *   block in bytes 0..3: the word a lane of the MFMA supplies over four
+ *   consecutive k-steps.
+ *   Padding bytes are 127 (the scale 2^0).
+ * orc_blocked_size: bytes of the blocked tensor (-1 for a bad shape). */
+int64_t orc_blocked_size(int64_t M, int64_t K);
+int orc_scales_to_blocked(const uint8_t *scales, int64_t M, int64_t K,
+                          uint8_t *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,9 @@ MUTANTS = {
     "no_subnormal_grid": ("if (e < f->emin)\n        e = f->emin;\n    double ulp", "double ulp"),
     "bf16_subnormal_exponent": ("ldexp((double)man, -133)", "ldexp((double)man, -134)"),
     "scale_from_first_element": ("else if (fabs(y[j]) > amax)", "else if (j == 0)"),
+    "blocked_lane_from_group_pair": ("int64_t lane = 32 * (g % 2) + i % 32;",
+                                     "int64_t lane = 32 * ((g % 8) / 4) + i % 32;"),
+    "blocked_byte_order": ("int64_t byte = (g % 8) / 2;", "int64_t byte = 3 - (g % 8) / 2;"),
     "exact_dequant_scale_bias": ("dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 127);",
                                  "dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 128);"),
     "exact_dequant_sign_dropped": ("dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 127);",

@@ -512,3 +512,60 @@ def test_matmul_one_hot_rows_pick_columns_of_b(orc, fmt):
     for i, k in enumerate(ks):
         for j in range(N):
             assert got[i, j] == textbook_row(fmt, b[j], bs[j], K)[k]
+
+
+# ---- blocked scale layout ----------------------------------------------------
+
+BLOCKED = os.path.join(os.path.dirname(__file__), "golden", "blocked_scales.json")
+
+
+def _distinct_scales(M, G):
+    # distinct per (row, group) where possible, never the padding value 127
+    return (1 + (np.arange(M * G) % 120)).astype(np.uint8).reshape(M, G)
+
+
+@pytest.mark.parametrize("case", json.load(open(BLOCKED))["cases"], ids=lambda c: f"{c['M']}x{c['K']}")
+def test_blocked_layout_hand_worked(orc, case):
+    M, K = case["M"], case["K"]
+    G = K // 32
+    s = _distinct_scales(M, G)
+    out = orc.scales_to_blocked(s, K)
+    assert out.size == case["size"] == orc.blocked_size(M, K)
+    for i, g, off in case["at"]:
+        assert out[off] == s[i, g], (i, g, off)
+    assert int((out == 127).sum()) == case["pad_bytes"]
+
+
+def test_blocked_layout_is_a_padded_permutation(orc):
+    rng = np.random.default_rng(3)
+    M, K = 100, 800
+    s = rng.integers(0, 256, (M, K // 32), dtype=np.uint8)
+    s[s == 127] = 0
+    out = orc.scales_to_blocked(s, K)
+    Mp, Gp = 128, 32
+    assert out.size == Mp * Gp
+    assert int((out == 127).sum()) == Mp * Gp - M * (K // 32)
+    assert np.array_equal(np.sort(out[out != 127]), np.sort(s.ravel()))
+
+
+def test_blocked_layout_words_serve_one_lane(orc):
+    # every 32-bit word holds four groups of one row, two groups apart
+    M, K = 64, 512
+    G = K // 32
+    rows = np.repeat(np.arange(M, dtype=np.int64)[:, None], G, 1)
+    groups = np.repeat(np.arange(G, dtype=np.int64)[None, :], M, 0)
+    code = (rows * G + groups).astype(np.int64)  # identify entries via two byte planes
+    lo = orc.scales_to_blocked((code % 251 + 1).astype(np.uint8), K)
+    hi = orc.scales_to_blocked((code // 251 + 1).astype(np.uint8), K)
+    ident = (hi.astype(np.int64) - 1) * 251 + (lo.astype(np.int64) - 1)
+    words = ident.reshape(-1, 4)
+    r, g = words // G, words % G
+    assert (r == r[:, :1]).all()
+    assert (np.diff(g, axis=1) == 2).all()
+    assert set(np.unique(g[:, 0] % 8)) == {0, 1}
+
+
+def test_blocked_size_rejects_bad_shapes(orc):
+    assert orc.blocked_size(4, 48) == -1
+    assert orc.blocked_size(-1, 32) == -1
+    assert orc.blocked_size(0, 32) == 0
