@@ -81,6 +81,11 @@ extern "C" {
 #define MX_ENULL (-5)   /* a required pointer is NULL                       */
 #define MX_EALIGN (-6)  /* a pointer breaks the alignment stated above      */
 #define MX_ELAUNCH (-7) /* the kernel launch failed (hipGetLastError)       */
+#define MX_ELAYOUT (-8) /* scale_layout is not one of MX_SCALES_*           */
+
+/* Scale layouts. */
+#define MX_SCALES_ROWMAJOR 0 /* [M x K/32] bytes, row-major, unpadded      */
+#define MX_SCALES_BLOCKED 1  /* the blocked layout described below         */
 
 /*
  * Fused quantize-dequantize ("use cute-dsl to speedup mxfp QDQ",
@@ -127,25 +132,59 @@ MX_API int mx_rotate(const void *src, int src_dtype, int64_t M, int64_t K,
                      const void *rot, int rot_size, float *dst);
 
 /*
+ * Blocked scale layout: the E8M0 scales in the order the gfx950 scaled
+ * matrix cores read them (32x32 tiles, 64-deep k-steps), so that a GEMM
+ * fetches each lane's scales with one coalesced 32-bit load per 256-deep
+ * k-span.  The pages pad and re-block the scale tensor for their GEMM
+ * ("Add QuTLASS support to vLLM", review of vllm/_custom_ops.py and
+ * vllm/qutlass_utils/utils.py: padded_rows x padded_cols, to_blocked;
+ * FlashInfer cute-dsl digest page: is_sf_swizzled_layout) but define it
+ * only for another GPU's matrix cores; this is the same idea for CDNA4.
+ *   - Rows are padded to a multiple of 32 and the K/32 groups of a row to a
+ *     multiple of 8.
+ *   - The scales form 256-byte blocks of 32 rows x 8 groups, stored in
+ *     row-major order over (row block, group block).
+ *   - In a block, 32-bit word l (l = 0..63) holds row l%32 of the block
+ *     and, in bytes 0..3, its groups h, 2+h, 4+h, 6+h (h = l/32).
+ *   - Padding bytes are 127 (the scale 2^0).
+ * mx_blocked_scales_bytes returns the size in bytes (MX_ESHAPE for a bad
+ * shape); blocked buffers must be 4-byte aligned.
+ */
+MX_API int64_t mx_blocked_scales_bytes(int64_t M, int64_t K);
+
+/* Re-blocks row-major [M x K/32] scales into the blocked layout (every byte
+ * of the blocked buffer is written, padding included). */
+MX_API int mx_scales_to_blocked(const uint8_t *scales, int64_t M, int64_t K,
+                                uint8_t *blocked);
+
+/* mx_quantize with the scales written directly in the blocked layout
+ * (padding included); codes as for mx_quantize. */
+MX_API int mx_quantize_blocked(int fmt, const void *src, int64_t M, int64_t K,
+                               const void *rot, int rot_size, uint8_t *codes,
+                               uint8_t *blocked_scales);
+
+/*
  * MX GEMM: c[M x N] (row-major) = alpha * A_dq . B_dq^T, where A is [M x K]
- * and B is [N x K], both in the layout mx_quantize writes (codes and
- * [rows x K/32] scales, K-contiguous: the "TN" operand order), on the CDNA4
- * scaled matrix cores.  Products of codes are exact, each product carries
- * the two scales of its groups, and accumulation is fp32; the result is
- * multiplied by alpha in fp32 and stored as out_dtype (bf16 by
+ * and B is [N x K], both with codes in the layout mx_quantize writes
+ * (K-contiguous: the "TN" operand order) and scales in scale_layout
+ * (MX_SCALES_ROWMAJOR or MX_SCALES_BLOCKED, both operands alike), on the
+ * CDNA4 scaled matrix cores.  Products of codes are exact, each product
+ * carries the two scales of its groups, and accumulation is fp32; the
+ * result is multiplied by alpha in fp32 and stored as out_dtype (bf16 by
  * nearest-even rounding, or fp32).  This is the consumer of the quantized
  * layout, with the call shape and check of the pages' MXFP4 GEMM ("Add
  * QuTLASS support to vLLM", Purpose: MXFP4 matmul kernel with alpha and
  * bf16 output; review of the MXFP4 test: compared with a_dq @ b_dq^T).
- *   codes      16-byte aligned; scales any alignment; c 16-byte aligned.
+ *   codes      16-byte aligned; c 16-byte aligned; row-major scales any
+ *              alignment, blocked scales 4-byte aligned.
  *   K == 0 stores zeros.  M <= 65535 * 128.
  *   A scale byte of 0xFF (NaN) or an E4M3 NaN code gives NaN in the
  *   affected outputs.
  */
 MX_API int mx_matmul(int fmt, const uint8_t *a_codes, const uint8_t *a_scales,
                      const uint8_t *b_codes, const uint8_t *b_scales,
-                     int64_t M, int64_t N, int64_t K, float alpha,
-                     int out_dtype, void *c);
+                     int scale_layout, int64_t M, int64_t N, int64_t K,
+                     float alpha, int out_dtype, void *c);
 
 /* Stream used by the calling thread's subsequent calls (a hipStream_t;
  * NULL = the default stream).  The setting is thread-local. */

@@ -27,6 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 E2M1, E4M3 = 0, 1
 BF16, F32 = 0, 1
+ROWMAJOR, BLOCKED = 0, 1
 _DTYPE = {torch.bfloat16: BF16, torch.float32: F32}
 
 _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -34,12 +35,17 @@ _lib.mx_qdq.argtypes = [_int, _vp, _int, _i64, _i64, _vp, _int, _vp]
 _lib.mx_quantize.argtypes = [_int, _vp, _i64, _i64, _vp, _int, _vp, _vp]
 _lib.mx_dequantize.argtypes = [_int, _vp, _vp, _i64, _i64, _int, _vp]
 _lib.mx_rotate.argtypes = [_vp, _int, _i64, _i64, _vp, _int, _vp]
-_lib.mx_matmul.argtypes = [_int, _vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_float, _int, _vp]
+_lib.mx_matmul.argtypes = [_int, _vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, ctypes.c_float, _int, _vp]
+_lib.mx_blocked_scales_bytes.argtypes = [_i64, _i64]
+_lib.mx_blocked_scales_bytes.restype = _i64
+_lib.mx_scales_to_blocked.argtypes = [_vp, _i64, _i64, _vp]
+_lib.mx_quantize_blocked.argtypes = [_int, _vp, _i64, _i64, _vp, _int, _vp, _vp]
 _lib.mx_set_stream.argtypes = [_vp]
 _lib.mx_get_stream.restype = _vp
 _lib.mx_status_string.argtypes = [_int]
 _lib.mx_status_string.restype = ctypes.c_char_p
-for _f in (_lib.mx_qdq, _lib.mx_quantize, _lib.mx_dequantize, _lib.mx_rotate, _lib.mx_matmul):
+for _f in (_lib.mx_qdq, _lib.mx_quantize, _lib.mx_dequantize, _lib.mx_rotate, _lib.mx_matmul,
+           _lib.mx_scales_to_blocked, _lib.mx_quantize_blocked):
     _f.restype = _int
 
 
@@ -146,18 +152,54 @@ def mx_rotate(src: torch.Tensor, rot: torch.Tensor, dst: torch.Tensor | None = N
     return dst
 
 
+def mx_blocked_scales_bytes(M: int, K: int) -> int:
+    n = _lib.mx_blocked_scales_bytes(M, K)
+    if n < 0:
+        raise MXError(n)
+    return n
+
+
+def mx_scales_to_blocked(scales: torch.Tensor, K: int, blocked: torch.Tensor | None = None) -> torch.Tensor:
+    """Row-major [M, K/32] scales -> the blocked layout (flat uint8)."""
+    M = scales.shape[0]
+    if blocked is None:
+        blocked = torch.empty(mx_blocked_scales_bytes(M, K), dtype=torch.uint8, device=scales.device)
+    _stream()
+    _call(_lib.mx_scales_to_blocked(_dev(scales, "scales"), M, K, _dev(blocked, "blocked")))
+    return blocked
+
+
+def mx_quantize_blocked(fmt: int, src: torch.Tensor, rot: torch.Tensor | None = None,
+                        codes: torch.Tensor | None = None, blocked: torch.Tensor | None = None):
+    """Quantize bf16 src [M, K] -> (codes, scales in the blocked layout)."""
+    M, K = _mk(src)
+    if src.dtype != torch.bfloat16:
+        raise TypeError("mx_quantize_blocked takes bfloat16 input")
+    if codes is None:
+        codes = torch.empty((M, K // 2 if fmt == E2M1 else K), dtype=torch.uint8, device=src.device)
+    if blocked is None:
+        blocked = torch.empty(mx_blocked_scales_bytes(M, K), dtype=torch.uint8, device=src.device)
+    rp, r = _rot(rot, src.dtype)
+    _stream()
+    _call(_lib.mx_quantize_blocked(fmt, _dev(src, "src"), M, K, rp, r, _dev(codes, "codes"),
+                                   _dev(blocked, "blocked")))
+    return codes, blocked
+
+
 def mx_matmul(fmt: int, a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor,
               b_scales: torch.Tensor, K: int, alpha: float = 1.0, dtype: torch.dtype = torch.bfloat16,
-              c: torch.Tensor | None = None):
-    """[M, N] = alpha * A_dq . B_dq^T from MX codes and scales (A [M, K], B [N, K])."""
-    M, N = a_scales.shape[0], b_scales.shape[0]
+              c: torch.Tensor | None = None, scale_layout: int = ROWMAJOR):
+    """[M, N] = alpha * A_dq . B_dq^T from MX codes and scales (A [M, K], B [N, K]);
+    the row counts come from the codes."""
+    M, N = a_codes.shape[0], b_codes.shape[0]
     if c is None:
         c = torch.empty((M, N), dtype=dtype, device=a_codes.device)
     if c.dtype not in _DTYPE or tuple(c.shape) != (M, N):
         raise ValueError("c must be a bfloat16 or float32 [M, N] tensor")
     _stream()
     _call(_lib.mx_matmul(fmt, _dev(a_codes, "a_codes"), _dev(a_scales, "a_scales"), _dev(b_codes, "b_codes"),
-                         _dev(b_scales, "b_scales"), M, N, K, float(alpha), _DTYPE[c.dtype], _dev(c, "c")))
+                         _dev(b_scales, "b_scales"), scale_layout, M, N, K, float(alpha), _DTYPE[c.dtype],
+                         _dev(c, "c")))
     return c
 
 

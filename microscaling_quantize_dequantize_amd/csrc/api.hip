@@ -111,20 +111,55 @@ MX_API int mx_rotate(const void *src, int src_dtype, int64_t M, int64_t K, const
                                  tl_stream));
 }
 
+MX_API int64_t mx_blocked_scales_bytes(int64_t M, int64_t K) {
+  if (check_shape(M, K) != MX_OK) return MX_ESHAPE;
+  return ((M + 31) / 32) * ((K / 32 + 7) / 8) * 256;
+}
+
+MX_API int mx_scales_to_blocked(const uint8_t *scales, int64_t M, int64_t K, uint8_t *blocked) {
+  int st;
+  if ((st = check_shape(M, K))) return st;
+  if (M == 0 || K == 0) return MX_OK;
+  if (!scales || !blocked) return MX_ENULL;
+  if (!aligned(blocked, 4)) return MX_EALIGN;
+  const mx::BlockedScales bl{M, K / 32, (K / 32 + 7) / 8};
+  return launched(mx::launch_scales_to_blocked(scales, bl, blocked, tl_stream));
+}
+
+MX_API int mx_quantize_blocked(int fmt, const void *src, int64_t M, int64_t K, const void *rot, int rot_size,
+                               uint8_t *codes, uint8_t *blocked_scales) {
+  int st;
+  if ((st = check_fmt(fmt)) || (st = check_shape(M, K)) || (st = check_rot(rot, rot_size, K, true)))
+    return st;
+  if (M == 0 || K == 0) return MX_OK;
+  if (!src || !codes || !blocked_scales) return MX_ENULL;
+  if (!aligned(src, 16) || !aligned(codes, 16) || !aligned(blocked_scales, 4) || (rot_size && !aligned(rot, 16)))
+    return MX_EALIGN;
+  const mx::BlockedScales bl{M, K / 32, (K / 32 + 7) / 8};
+  const int64_t n = M * K;
+  if (rot_size == 0)
+    return launched(mx::launch_unrot(fmt, mx::OP_QUANT, MX_DTYPE_BF16, src, nullptr, codes, blocked_scales, n,
+                                     tl_stream, &bl));
+  return launched(mx::launch_rot(fmt, mx::OP_QUANT, MX_DTYPE_BF16, src, rot, rot_size, nullptr, codes,
+                                 blocked_scales, n, tl_stream, &bl));
+}
+
 MX_API int mx_matmul(int fmt, const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
-                     const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, float alpha, int out_dtype,
-                     void *c) {
+                     const uint8_t *b_scales, int scale_layout, int64_t M, int64_t N, int64_t K, float alpha,
+                     int out_dtype, void *c) {
   int st;
   if ((st = check_fmt(fmt)) || (st = check_dtype(out_dtype)) || (st = check_shape(M, K)) ||
       (st = check_shape(N, K)))
     return st;
+  if (scale_layout != MX_SCALES_ROWMAJOR && scale_layout != MX_SCALES_BLOCKED) return MX_ELAYOUT;
   if (M > ((int64_t)65535 << 7) || (N + 127) / 128 > (int64_t)INT32_MAX) return MX_ESHAPE;  // grid limits
   if (M == 0 || N == 0) return MX_OK;
   if (!c) return MX_ENULL;
   if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return MX_ENULL;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(c, 16)) return MX_EALIGN;
-  return launched(
-      mx::launch_gemm(fmt, a_codes, a_scales, b_codes, b_scales, M, N, K, alpha, out_dtype, c, tl_stream));
+  if (scale_layout == MX_SCALES_BLOCKED && (!aligned(a_scales, 4) || !aligned(b_scales, 4))) return MX_EALIGN;
+  return launched(mx::launch_gemm(fmt, a_codes, a_scales, b_codes, b_scales, scale_layout, M, N, K, alpha,
+                                  out_dtype, c, tl_stream));
 }
 
 MX_API void mx_set_stream(void *stream) { tl_stream = (hipStream_t)stream; }
@@ -141,6 +176,7 @@ MX_API const char *mx_status_string(int status) {
     case MX_ENULL: return "a required pointer is NULL";
     case MX_EALIGN: return "misaligned pointer (16 bytes; scales 4 bytes)";
     case MX_ELAUNCH: return "kernel launch failed";
+    case MX_ELAYOUT: return "invalid scale layout (expected MX_SCALES_ROWMAJOR or MX_SCALES_BLOCKED)";
     default: return "unknown status";
   }
 }

@@ -29,7 +29,10 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int GT = 256, BM = 128, BN = 128, BK = 128;
 
-template <int FMT, int OUT>
+// SL 0: row-major [rows x K/32] scales, staged through LDS per k-slice;
+// SL 1: the blocked layout, where a lane's word for its row block and
+// 256-deep k-span is one coalesced 32-bit load.
+template <int FMT, int OUT, int SL>
 __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                                                  const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
                                                  int64_t M, int64_t N, int64_t K, float alpha,
@@ -49,6 +52,7 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const int64_t rowbytes = FMT == 0 ? K / 2 : K;
   const int64_t groups = K / 32;
+  const int64_t gblocks = (groups + 7) / 8;
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -69,12 +73,23 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       *(u32x4 *)(sB + row * LDR + 16 * c) = vb;
     }
     // rows past the end and groups past K hold zero codes; any finite scale will do
+    unsigned wa[2] = {0x7F7F7F7Fu, 0x7F7F7F7Fu}, wb[2] = {0x7F7F7F7Fu, 0x7F7F7F7Fu};
+    if (SL == 0) {
 #pragma unroll
-    for (int it = 0; it < BM * GS / GT; ++it) {
-      const int idx = tid + it * GT, row = idx / GS, gg = idx % GS;
-      const int64_t g = k0 / 32 + gg;
-      sSA[idx] = (m0 + row < M && g < groups) ? As[(m0 + row) * groups + g] : (uint8_t)127;
-      sSB[idx] = (n0 + row < N && g < groups) ? Bs[(n0 + row) * groups + g] : (uint8_t)127;
+      for (int it = 0; it < BM * GS / GT; ++it) {
+        const int idx = tid + it * GT, row = idx / GS, gg = idx % GS;
+        const int64_t g = k0 / 32 + gg;
+        sSA[idx] = (m0 + row < M && g < groups) ? As[(m0 + row) * groups + g] : (uint8_t)127;
+        sSB[idx] = (n0 + row < N && g < groups) ? Bs[(n0 + row) * groups + g] : (uint8_t)127;
+      }
+    } else {
+      // row blocks exist up to the one holding the last row; padding groups hold 127
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t ra = m0 + wm + 32 * i, rb = n0 + wn + 32 * i;
+        if (ra < M) wa[i] = ((const unsigned *)As)[((ra >> 5) * gblocks + (k0 >> 8)) * 64 + lane];
+        if (rb < N) wb[i] = ((const unsigned *)Bs)[((rb >> 5) * gblocks + (k0 >> 8)) * 64 + lane];
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -96,8 +111,14 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
         }
         fa[i] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
         fb[i] = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-        sa[i] = sSA[ra * GS + 2 * s + h];  // this lane's group of the 64-deep step
-        sb[i] = sSB[rb * GS + 2 * s + h];
+        if (SL == 0) {
+          sa[i] = sSA[ra * GS + 2 * s + h];  // this lane's group of the 64-deep step
+          sb[i] = sSB[rb * GS + 2 * s + h];
+        } else {
+          const int sh = 8 * ((int)((k0 >> 6) & 3) + s);  // k-step within the 256-deep span
+          sa[i] = (int)((wa[i] >> sh) & 0xFFu);
+          sb[i] = (int)((wb[i] >> sh) & 0xFFu);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -126,13 +147,21 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
     }
 }
 
+template <int SL>
+static void run_gemm(int fmt, int out_dtype, dim3 grid, const uint8_t *a, const uint8_t *as, const uint8_t *b,
+                     const uint8_t *bs, int64_t M, int64_t N, int64_t K, float alpha, void *c, hipStream_t st) {
+  if (fmt == 0 && out_dtype == 0) k_mx_gemm<0, 0, SL><<<grid, GT, 0, st>>>(a, as, b, bs, M, N, K, alpha, c);
+  else if (fmt == 0) k_mx_gemm<0, 1, SL><<<grid, GT, 0, st>>>(a, as, b, bs, M, N, K, alpha, c);
+  else if (out_dtype == 0) k_mx_gemm<1, 0, SL><<<grid, GT, 0, st>>>(a, as, b, bs, M, N, K, alpha, c);
+  else k_mx_gemm<1, 1, SL><<<grid, GT, 0, st>>>(a, as, b, bs, M, N, K, alpha, c);
+}
+
 hipError_t launch_gemm(int fmt, const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs,
-                       int64_t M, int64_t N, int64_t K, float alpha, int out_dtype, void *c, hipStream_t st) {
+                       int scale_layout, int64_t M, int64_t N, int64_t K, float alpha, int out_dtype, void *c,
+                       hipStream_t st) {
   const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  if (fmt == 0 && out_dtype == 0) k_mx_gemm<0, 0><<<grid, GT, 0, st>>>(a, as, b, bs, M, N, K, alpha, c);
-  else if (fmt == 0) k_mx_gemm<0, 1><<<grid, GT, 0, st>>>(a, as, b, bs, M, N, K, alpha, c);
-  else if (out_dtype == 0) k_mx_gemm<1, 0><<<grid, GT, 0, st>>>(a, as, b, bs, M, N, K, alpha, c);
-  else k_mx_gemm<1, 1><<<grid, GT, 0, st>>>(a, as, b, bs, M, N, K, alpha, c);
+  if (scale_layout == 0) run_gemm<0>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
+  else run_gemm<1>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
   return hipGetLastError();
 }
 

@@ -186,6 +186,38 @@ __device__ __forceinline__ unsigned bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// ---- blocked scale layout ---------------------------------------------------
+// The operand order of the 32x32x64 scaled MFMA: rows padded to 32, groups
+// to 8; 256-byte blocks of 32 rows x 8 groups in row-major block order; word
+// l of a block holds row l%32 and, in bytes 0..3, groups h, 2+h, 4+h, 6+h of
+// the block (h = l/32); padding bytes are 127 (2^0).
+struct BlockedScales {
+  int64_t rows, groups, gblocks;  // M, K/32, ceil(K/32 / 8)
+};
+
+__device__ __forceinline__ int64_t blocked_offset(int64_t i, int64_t g, int64_t gblocks) {
+  return ((((i >> 5) * gblocks) + (g >> 3)) << 8) + 4 * (32 * (g & 1) + (i & 31)) + ((g & 7) >> 1);
+}
+
+// Writes the padding bytes (groups past K of every row, then the rows past M)
+// with a grid-stride loop over threads t of nt.
+__device__ __forceinline__ void write_blocked_pads(uint8_t *__restrict__ out, const BlockedScales &bl, int64_t t,
+                                                   int64_t nt) {
+  const int64_t gp = bl.gblocks * 8, per_row = gp - bl.groups;
+  const int64_t a = bl.rows * per_row, total = a + (((bl.rows + 31) & ~(int64_t)31) - bl.rows) * gp;
+  for (; t < total; t += nt) {
+    int64_t i, g;
+    if (t < a) {
+      i = t / per_row;
+      g = bl.groups + (t - i * per_row);
+    } else {
+      i = bl.rows + (t - a) / gp;
+      g = (t - a) % gp;
+    }
+    out[blocked_offset(i, g, bl.gblocks)] = 127;
+  }
+}
+
 // ---- cross-lane helpers ---------------------------------------------------
 
 // DPP controls (gfx9 encodings).

@@ -148,11 +148,13 @@ __device__ __forceinline__ void group_fp8_bytes(const unsigned c[4], unsigned sb
 }
 
 // bf16 source, OP_QDQ (bf16 out) or OP_QUANT, staged through LDS.
-template <int FMT, int OP, int RB, int THREADS>
+// SL (OP_QUANT only): 0 = row-major scales, 1 = the blocked layout `bl`.
+template <int FMT, int OP, int RB, int THREADS, int SL>
 __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict__ src,
                                                       const uint16_t *__restrict__ rot, int r,
                                                       void *__restrict__ dst, uint8_t *__restrict__ codes,
-                                                      uint8_t *__restrict__ scales, int64_t n_blk) {
+                                                      uint8_t *__restrict__ scales, int64_t n_blk,
+                                                      BlockedScales bl) {
   constexpr int NJT = RB / 32, NKB = RB / 16;
   constexpr int C = RB / 8;           // 16-byte input pieces per block
   constexpr int TP = 32 * C;          // input pieces per tile (= 64 * NKB)
@@ -182,6 +184,8 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
     }
   }
   __syncthreads();
+  if (SL == 1)
+    write_blocked_pads(scales, bl, (int64_t)blockIdx.x * THREADS + threadIdx.x, (int64_t)gridDim.x * THREADS);
   const uint16_t *Rs = (const uint16_t *)&sT[0][0];
   // A fragment (jt, kb) of lane ln: Reff[t][j] for j = 32*jt + ln%32 and
   // t = 16*kb + 8*(ln/32) + i, i = 0..7.
@@ -264,7 +268,12 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
         }
       }
     }
-    if (OP == OP_QUANT && h == 0 && blk < n_blk) {
+    if (OP == OP_QUANT && SL == 1 && h == 0 && blk < n_blk) {
+      // a block lies in one row: its groups are g0 .. g0 + NJT - 1
+      const int64_t gf0 = blk * NJT, i = gf0 / bl.groups, g0 = gf0 - i * bl.groups;
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) scales[blocked_offset(i, g0 + jt, bl.gblocks)] = (uint8_t)(sbw >> (8 * jt));
+    } else if (OP == OP_QUANT && h == 0 && blk < n_blk) {
       if (NJT == 4) *(unsigned *)(scales + blk * 4) = sbw;
       else if (NJT == 2) *(uint16_t *)(scales + blk * 2) = (uint16_t)sbw;
       else scales[blk] = (uint8_t)sbw;
@@ -439,12 +448,19 @@ static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
 
 template <int FMT, int OP, int RB>
 static void run_staged(const void *src, const void *rot, int r, void *dst, uint8_t *codes, uint8_t *scales,
-                       int64_t n, hipStream_t st) {
+                       int64_t n, hipStream_t st, const BlockedScales *bl) {
   using Cfg = StagedCfg<RB>;
   const int64_t n_blk = n / RB;
   const unsigned g = persistent_grid((n_blk + 31) / 32, Cfg::threads / 64, Cfg::per_cu);
-  k_rot_bf16<FMT, OP, RB, Cfg::threads><<<g, Cfg::threads, 0, st>>>(
-      (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk);
+  if constexpr (OP == OP_QUANT) {
+    if (bl != nullptr) {
+      k_rot_bf16<FMT, OP, RB, Cfg::threads, 1><<<g, Cfg::threads, 0, st>>>(
+          (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, *bl);
+      return;
+    }
+  }
+  k_rot_bf16<FMT, OP, RB, Cfg::threads, 0><<<g, Cfg::threads, 0, st>>>(
+      (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, BlockedScales{0, 0, 0});
 }
 
 template <int FMT, int OP, int RB>
@@ -459,12 +475,12 @@ static void run_direct(int dtype, const void *src, const void *rot, int r, void 
 
 template <int FMT, int OP>
 static void dispatch_rb(int dtype, const void *src, const void *rot, int r, void *dst, uint8_t *codes,
-                        uint8_t *scales, int64_t n, hipStream_t st) {
+                        uint8_t *scales, int64_t n, hipStream_t st, const BlockedScales *bl) {
   const int rb = r < 32 ? 32 : r;
   if (dtype == 0 && OP != OP_ROTATE) {
-    if (rb == 32) run_staged<FMT, OP, 32>(src, rot, r, dst, codes, scales, n, st);
-    else if (rb == 64) run_staged<FMT, OP, 64>(src, rot, r, dst, codes, scales, n, st);
-    else run_staged<FMT, OP, 128>(src, rot, r, dst, codes, scales, n, st);
+    if (rb == 32) run_staged<FMT, OP, 32>(src, rot, r, dst, codes, scales, n, st, bl);
+    else if (rb == 64) run_staged<FMT, OP, 64>(src, rot, r, dst, codes, scales, n, st, bl);
+    else run_staged<FMT, OP, 128>(src, rot, r, dst, codes, scales, n, st, bl);
   } else if (OP != OP_QUANT) {
     if (rb == 32) run_direct<FMT, OP, 32>(dtype, src, rot, r, dst, n, st);
     else if (rb == 64) run_direct<FMT, OP, 64>(dtype, src, rot, r, dst, n, st);
@@ -473,15 +489,15 @@ static void dispatch_rb(int dtype, const void *src, const void *rot, int r, void
 }
 
 hipError_t launch_rot(int fmt, int op, int dtype, const void *src, const void *rot, int r, void *dst,
-                      uint8_t *codes, uint8_t *scales, int64_t n, hipStream_t st) {
+                      uint8_t *codes, uint8_t *scales, int64_t n, hipStream_t st, const BlockedScales *bl) {
   if (op == OP_ROTATE) {
-    dispatch_rb<0, OP_ROTATE>(dtype, src, rot, r, dst, codes, scales, n, st);
+    dispatch_rb<0, OP_ROTATE>(dtype, src, rot, r, dst, codes, scales, n, st, nullptr);
   } else if (fmt == 0) {
-    if (op == OP_QDQ) dispatch_rb<0, OP_QDQ>(dtype, src, rot, r, dst, codes, scales, n, st);
-    else dispatch_rb<0, OP_QUANT>(dtype, src, rot, r, dst, codes, scales, n, st);
+    if (op == OP_QDQ) dispatch_rb<0, OP_QDQ>(dtype, src, rot, r, dst, codes, scales, n, st, nullptr);
+    else dispatch_rb<0, OP_QUANT>(dtype, src, rot, r, dst, codes, scales, n, st, bl);
   } else {
-    if (op == OP_QDQ) dispatch_rb<1, OP_QDQ>(dtype, src, rot, r, dst, codes, scales, n, st);
-    else dispatch_rb<1, OP_QUANT>(dtype, src, rot, r, dst, codes, scales, n, st);
+    if (op == OP_QDQ) dispatch_rb<1, OP_QDQ>(dtype, src, rot, r, dst, codes, scales, n, st, nullptr);
+    else dispatch_rb<1, OP_QUANT>(dtype, src, rot, r, dst, codes, scales, n, st, bl);
   }
   return hipGetLastError();
 }

@@ -35,14 +35,17 @@ __device__ __forceinline__ unsigned piece_amax_bf16(u32x4 w) {
 }
 
 // OP_QDQ: dst (bf16) = dequantized values.  OP_QUANT: codes + scales.
-template <int FMT, int OP, int THREADS, int UNROLL>
+// SL (OP_QUANT only): 0 = row-major scales, 1 = the blocked layout `bl`.
+template <int FMT, int OP, int THREADS, int UNROLL, int SL>
 __global__ __launch_bounds__(THREADS) void k_unrot_bf16(const u32x4 *__restrict__ src,
                                                         u32x4 *__restrict__ dst,
                                                         uint8_t *__restrict__ codes,
                                                         uint8_t *__restrict__ scales,
-                                                        int64_t n_pieces) {
+                                                        int64_t n_pieces, BlockedScales bl) {
   constexpr int64_t SWEEP = THREADS * UNROLL;  // pieces per block per sweep
   const int tid = threadIdx.x;
+  if (SL == 1)
+    write_blocked_pads(scales, bl, (int64_t)blockIdx.x * THREADS + tid, (int64_t)gridDim.x * THREADS);
   for (int64_t sweep = blockIdx.x; sweep * SWEEP < n_pieces; sweep += gridDim.x) {
     const int64_t base = sweep * SWEEP + tid;
     u32x4 w[UNROLL];
@@ -85,6 +88,14 @@ __global__ __launch_bounds__(THREADS) void k_unrot_bf16(const u32x4 *__restrict_
           u32x2 c = fp8_from_bf16x8(x, sc);
           if (sb == 255u) c = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
           if (p < n_pieces) __builtin_nontemporal_store(c, (u32x2 *)codes + p);
+        }
+        if (SL == 1) {
+          // blocked layout: the group's first lane stores its byte
+          if ((tid & 3) == 0 && p < n_pieces) {
+            const int64_t gf = p >> 2, i = gf / bl.groups;
+            scales[blocked_offset(i, gf - i * bl.groups, bl.gblocks)] = (uint8_t)sb;
+          }
+          continue;
         }
         // Scale bytes: lanes 16k..16k+15 hold 4 consecutive groups; gather
         // the 4 bytes into lane 16k (row rotations by 4 and 8) and store one
@@ -209,7 +220,7 @@ constexpr int QNT_T = 128, QNT_U = 2;
 constexpr int DEQ_T = 128;
 
 hipError_t launch_unrot(int fmt, int op, int dtype, const void *src, void *dst, uint8_t *codes,
-                        uint8_t *scales, int64_t n, hipStream_t stream) {
+                        uint8_t *scales, int64_t n, hipStream_t stream, const BlockedScales *bl) {
   const u32x4 *s = (const u32x4 *)src;
   if (dtype == 1) {  // fp32, QDQ only
     const int64_t np = n / 4;
@@ -220,14 +231,24 @@ hipError_t launch_unrot(int fmt, int op, int dtype, const void *src, void *dst, 
   }
   const int64_t np = n / 8;
   u32x4 *d = (u32x4 *)dst;
+  const BlockedScales none{0, 0, 0};
   if (op == OP_QDQ) {
     const unsigned g = grid_for(np, QDQ_T * QDQ_U);
-    if (fmt == 0) k_unrot_bf16<0, OP_QDQ, QDQ_T, QDQ_U><<<g, QDQ_T, 0, stream>>>(s, d, nullptr, nullptr, np);
-    else k_unrot_bf16<1, OP_QDQ, QDQ_T, QDQ_U><<<g, QDQ_T, 0, stream>>>(s, d, nullptr, nullptr, np);
+    if (fmt == 0) k_unrot_bf16<0, OP_QDQ, QDQ_T, QDQ_U, 0><<<g, QDQ_T, 0, stream>>>(s, d, nullptr, nullptr, np, none);
+    else k_unrot_bf16<1, OP_QDQ, QDQ_T, QDQ_U, 0><<<g, QDQ_T, 0, stream>>>(s, d, nullptr, nullptr, np, none);
   } else {
     const unsigned g = grid_for(np, QNT_T * QNT_U);
-    if (fmt == 0) k_unrot_bf16<0, OP_QUANT, QNT_T, QNT_U><<<g, QNT_T, 0, stream>>>(s, nullptr, codes, scales, np);
-    else k_unrot_bf16<1, OP_QUANT, QNT_T, QNT_U><<<g, QNT_T, 0, stream>>>(s, nullptr, codes, scales, np);
+    if (bl == nullptr) {
+      if (fmt == 0)
+        k_unrot_bf16<0, OP_QUANT, QNT_T, QNT_U, 0><<<g, QNT_T, 0, stream>>>(s, nullptr, codes, scales, np, none);
+      else
+        k_unrot_bf16<1, OP_QUANT, QNT_T, QNT_U, 0><<<g, QNT_T, 0, stream>>>(s, nullptr, codes, scales, np, none);
+    } else {
+      if (fmt == 0)
+        k_unrot_bf16<0, OP_QUANT, QNT_T, QNT_U, 1><<<g, QNT_T, 0, stream>>>(s, nullptr, codes, scales, np, *bl);
+      else
+        k_unrot_bf16<1, OP_QUANT, QNT_T, QNT_U, 1><<<g, QNT_T, 0, stream>>>(s, nullptr, codes, scales, np, *bl);
+    }
   }
   return hipGetLastError();
 }

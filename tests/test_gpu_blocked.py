@@ -1,0 +1,127 @@
+"""GPU parity of the blocked scale layout: the rearrangement kernel, the
+quantize that writes blocked scales directly, and the GEMM that reads them.
+
+Bars: the blocked bytes are bit-exact against the oracle's rearrangement of
+the oracle's scales (unrotated path), every padding byte included; on the
+rotated path, where scales may differ from the oracle at rounding ties (the
+band test of the rotated parity file covers those), the fused blocked
+output must equal the library's own row-major output re-blocked; the GEMM
+with blocked scales must equal, bit for bit, the GEMM with row-major scales.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from _parity import E2M1, E4M3, THREADS, assert_bits_equal, bits_of, gemm_error_bound, to_gpu_bf16
+from microscaling_quantize_dequantize_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from microscaling_quantize_dequantize_amd import binding
+    return binding
+
+
+def gpu_u8(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def poisoned(mx, M, K):
+    import torch
+    return torch.full((mx.mx_blocked_scales_bytes(M, K),), 0xFF, dtype=torch.uint8, device="cuda")
+
+
+SHAPES = [(1, 32), (2, 64), (33, 288), (77, 224), (100, 800), (256, 4096), (130, 57344 // 8)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_scales_to_blocked_matches_oracle(mx, shape):
+    import torch
+    M, K = shape
+    rng = np.random.default_rng([M, K])
+    s = rng.integers(0, 256, (M, K // 32), dtype=np.uint8)
+    out = poisoned(mx, M, K)
+    mx.mx_scales_to_blocked(gpu_u8(s), K, blocked=out)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits_of(out), oracle.scales_to_blocked(s, K), f"blocked {shape}")
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+@pytest.mark.parametrize("shape", [(77, 224), (33, 288), (64, 4096), (200, 1056)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_quantize_blocked_matches_oracle(mx, fmt, shape):
+    import torch
+    M, K = shape
+    x = W.random_bf16((M, K), seed=M + K)
+    out = poisoned(mx, M, K)
+    codes, blocked = mx.mx_quantize_blocked(fmt, to_gpu_bf16(x), blocked=out)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.quantize(fmt, x, threads=THREADS)
+    assert_bits_equal(bits_of(codes), c_ref, f"codes fmt{fmt} {shape}")
+    assert_bits_equal(bits_of(blocked), oracle.scales_to_blocked(s_ref, K), f"blocked scales fmt{fmt} {shape}")
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+@pytest.mark.parametrize("r,shape", [(16, (77, 224)), (32, (33, 288)), (64, (45, 384)), (128, (129, 1152))],
+                         ids=lambda v: str(v))
+def test_quantize_blocked_rotated_equals_rowmajor(mx, fmt, r, shape):
+    import torch
+    M, K = shape
+    x = to_gpu_bf16(W.random_bf16((M, K), seed=7 * r + M))
+    R = to_gpu_bf16(W.hadamard_rotation(r))
+    codes_b, blocked = mx.mx_quantize_blocked(fmt, x, rot=R, blocked=poisoned(mx, M, K))
+    codes, scales = mx.mx_quantize(fmt, x, rot=R)
+    reblocked = mx.mx_scales_to_blocked(scales, K, blocked=poisoned(mx, M, K))
+    torch.cuda.synchronize()
+    assert_bits_equal(bits_of(codes_b), bits_of(codes), f"rotated codes fmt{fmt} r{r}")
+    assert_bits_equal(bits_of(blocked), bits_of(reblocked), f"rotated blocked fmt{fmt} r{r}")
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+@pytest.mark.parametrize("shape", [(128, 128, 256), (200, 136, 160), (33, 257, 96), (256, 320, 2080)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_matmul_blocked_equals_rowmajor(mx, fmt, shape):
+    import torch
+    M, N, K = shape
+    xa = W.random_bf16((M, K), seed=11 + M)
+    xb = W.random_bf16((N, K), seed=13 + N, scale=0.05)
+    a, sa = oracle.quantize(fmt, xa, threads=THREADS)
+    b, sb = oracle.quantize(fmt, xb, threads=THREADS)
+    ga, gb = gpu_u8(a), gpu_u8(b)
+    c_row = mx.mx_matmul(fmt, ga, gpu_u8(sa), gb, gpu_u8(sb), K, dtype=torch.float32)
+    c_blk = mx.mx_matmul(fmt, ga, gpu_u8(oracle.scales_to_blocked(sa, K)), gb,
+                         gpu_u8(oracle.scales_to_blocked(sb, K)), K, dtype=torch.float32,
+                         scale_layout=mx.BLOCKED)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits_of(c_blk), bits_of(c_row), f"gemm blocked fmt{fmt} {shape}")
+    ref = oracle.matmul(fmt, a, sa, b, sb, K)
+    bound = gemm_error_bound(fmt, oracle.dequantize_f64(fmt, a, sa, K), oracle.dequantize_f64(fmt, b, sb, K))
+    err = np.abs(c_blk.cpu().numpy().astype(np.float64) - ref)
+    assert (err <= bound + 2.0 ** -24 * np.abs(ref)).all()
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_quantize_blocked_full_size(mx, fmt):
+    """The down-projection activation shape [8192 x 28672] with rotation 128,
+    in the launch configuration of the timed GEMM consumer: the fused blocked
+    output equals the re-blocked row-major output everywhere, and the
+    unrotated blocked scales of rows 0-63 match the oracle's."""
+    import torch
+    M, K = 8192, 28672
+    x_bits = W.generate("c4")
+    x = to_gpu_bf16(x_bits)
+    R = to_gpu_bf16(W.hadamard_rotation(128))
+    _, blocked = mx.mx_quantize_blocked(fmt, x, rot=R, blocked=poisoned(mx, M, K))
+    _, scales = mx.mx_quantize(fmt, x, rot=R)
+    reblocked = mx.mx_scales_to_blocked(scales, K, blocked=poisoned(mx, M, K))
+    _, blocked0 = mx.mx_quantize_blocked(fmt, x, blocked=poisoned(mx, M, K))
+    torch.cuda.synchronize()
+    assert torch.equal(blocked, reblocked)
+    _, s_ref = oracle.quantize(fmt, x_bits[:64], threads=THREADS)
+    head = 2 * ((K // 32 + 7) // 8) * 256  # the first two row blocks
+    assert_bits_equal(bits_of(blocked0[:head]), oracle.scales_to_blocked(s_ref, K), f"full-size head fmt{fmt}")
