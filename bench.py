@@ -234,24 +234,47 @@ def main():
                        "GBps": round(4 * n / (avg * 1e-3) / 1e9, 1),
                        "frac_of_peak": round(4 * n / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)})
     del deq_out
+    # blocked scale layout: the step's quantize with blocked scales, and the
+    # re-blocking of row-major scales
+    blk = torch.empty(mx.mx_blocked_scales_bytes(M, K), dtype=torch.uint8, device=dev)
+    for fmt, r in ((0, 0), (0, 128), (1, 0)):
+        R = rots[r][1] if r else None
+        mx.mx_quantize_blocked(fmt, x, rot=R, codes=codes[fmt], blocked=blk)
+        avg, mn = timed(lambda: mx.mx_quantize_blocked(fmt, x, rot=R, codes=codes[fmt], blocked=blk), 10)
+        bts = n * (2.0 + (0.5 if fmt == 0 else 1.0)) + blk.numel()
+        extras.append({"kernel": f"quantize_blocked_{'mxfp4' if fmt == 0 else 'mxfp8'}_rot{r}", "bytes": int(bts),
+                       "avg_us": round(avg * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                       "GBps": round(bts / (avg * 1e-3) / 1e9, 1),
+                       "frac_of_peak": round(bts / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)})
+    mx.mx_quantize(0, x, codes=codes[0], scales=scales)
+    avg, mn = timed(lambda: mx.mx_scales_to_blocked(scales, K, blocked=blk), 10)
+    bts = scales.numel() + blk.numel()
+    extras.append({"kernel": "scales_to_blocked", "bytes": int(bts), "avg_us": round(avg * 1e3, 2),
+                   "min_us": round(mn * 1e3, 2), "GBps": round(bts / (avg * 1e-3) / 1e9, 1),
+                   "frac_of_peak": round(bts / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)})
+    del blk
     # GEMM consumer: the layer's bytes read as two [8192 x 28672] operands
     # (activations and weights of a down projection), quantized, then
-    # C[8192 x 8192] (bf16) = A_dq . B_dq^T on the scaled matrix cores
+    # C[8192 x 8192] (bf16) = A_dq . B_dq^T on the scaled matrix cores, with
+    # row-major and with blocked scales
     gm, gk = 8192, n // (2 * 8192)
     gx = x.view(2 * gm, gk)
     gc = torch.empty((gm, gm), dtype=torch.bfloat16, device=dev)
     for fmt in (0, 1):
         cq, sq = mx.mx_quantize(fmt, gx)
         a, b_, sa, sb = cq[:gm], cq[gm:], sq[:gm], sq[gm:]
-        for _ in range(2):
-            mx.mx_matmul(fmt, a, sa, b_, sb, gk, c=gc)
-        avg, mn = timed(lambda: mx.mx_matmul(fmt, a, sa, b_, sb, gk, c=gc), 10)
-        tflops = 2.0 * gm * gm * gk / (avg * 1e-3) / 1e12
-        extras.append({"kernel": f"matmul_{'mxfp4' if fmt == 0 else 'mxfp8'}_{gm}x{gm}x{gk}_bf16out",
-                       "flops": 2 * gm * gm * gk, "avg_us": round(avg * 1e3, 2), "min_us": round(mn * 1e3, 2),
-                       "TFLOPs": round(tflops, 1), "bound": "mfma", "peak_TFLOPs": GEMM_PEAK_TFLOPS[fmt],
-                       "frac_of_peak": round(tflops / GEMM_PEAK_TFLOPS[fmt], 4)})
-        del cq, sq, a, b_, sa, sb
+        ba, bb = mx.mx_scales_to_blocked(sa, gk), mx.mx_scales_to_blocked(sb, gk)
+        for layout, (xa, xb) in ((mx.ROWMAJOR, (sa, sb)), (mx.BLOCKED, (ba, bb))):
+            for _ in range(2):
+                mx.mx_matmul(fmt, a, xa, b_, xb, gk, c=gc, scale_layout=layout)
+            avg, mn = timed(lambda: mx.mx_matmul(fmt, a, xa, b_, xb, gk, c=gc, scale_layout=layout), 10)
+            tflops = 2.0 * gm * gm * gk / (avg * 1e-3) / 1e12
+            extras.append({"kernel": f"matmul_{'mxfp4' if fmt == 0 else 'mxfp8'}_{gm}x{gm}x{gk}_bf16out"
+                                     f"{'_blocked' if layout == mx.BLOCKED else ''}",
+                           "flops": 2 * gm * gm * gk, "avg_us": round(avg * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                           "TFLOPs": round(tflops, 1), "bound": "mfma", "peak_TFLOPs": GEMM_PEAK_TFLOPS[fmt],
+                           "frac_of_peak": round(tflops / GEMM_PEAK_TFLOPS[fmt], 4)})
+        del cq, sq, a, b_, sa, sb, ba, bb
     del gc
 
     # measured copy ceiling: device-to-device copy of the same layer

@@ -123,6 +123,7 @@ MX_API int mx_scales_to_blocked(const uint8_t *scales, int64_t M, int64_t K, uin
   if (!scales || !blocked) return MX_ENULL;
   if (!aligned(blocked, 4)) return MX_EALIGN;
   const mx::BlockedScales bl{M, K / 32, (K / 32 + 7) / 8};
+  if ((M + 31) / 32 > (int64_t)INT32_MAX || (bl.gblocks + 7) / 8 > 65535) return MX_ESHAPE;  // grid limits
   return launched(mx::launch_scales_to_blocked(scales, bl, blocked, tl_stream));
 }
 

@@ -9,32 +9,50 @@
 namespace mx {
 
 constexpr int BT = 256;
+constexpr int SPAN = 8;        // group blocks per workgroup (64 groups)
+constexpr int TROW = 8 * SPAN + 4;  // LDS row stride in bytes (17 words: conflict-free columns)
 
-// One thread per 32-bit word of the output: word l of block b holds row
-// 32*(b / gblocks) + l%32 and groups 8*(b % gblocks) + 2j + l/32, j = 0..3.
+// One workgroup per (row block, span of 8 group blocks): the 32 rows x 64
+// groups are read row-wise (consecutive threads, consecutive bytes of a
+// row) into LDS, then written as 8 whole 256-byte blocks, one 32-bit word
+// per thread: word l of a block holds row l%32 and groups 2j + l/32.
 __global__ __launch_bounds__(BT) void k_scales_to_blocked(const uint8_t *__restrict__ scales, BlockedScales bl,
-                                                          unsigned *__restrict__ out, int64_t n_words) {
-  for (int64_t d = (int64_t)blockIdx.x * BT + threadIdx.x; d < n_words; d += (int64_t)gridDim.x * BT) {
-    const int64_t b = d >> 6, rb = b / bl.gblocks, kb = b - rb * bl.gblocks;
-    const int l = (int)(d & 63);
-    const int64_t row = 32 * rb + (l & 31);
-    unsigned w = 0;
+                                                          unsigned *__restrict__ out) {
+  __shared__ __attribute__((aligned(4))) uint8_t tile[32 * TROW];
+  const int t = threadIdx.x;
+  const int64_t rb = blockIdx.x, kb0 = (int64_t)blockIdx.y * SPAN;
+  {
+    const int r = t >> 3, c = t & 7;  // row of the block, 8-group chunk of the span
+    const int64_t row = 32 * rb + r, g0 = 8 * (kb0 + c);
+    if ((bl.groups & 7) == 0 && ((uintptr_t)scales & 7) == 0 && row < bl.rows && g0 < bl.groups) {
+      // a whole, 8-byte aligned chunk; LDS rows are 4-byte aligned
+      const u32x2 v = *(const u32x2 *)(scales + row * bl.groups + g0);
+      unsigned *d = (unsigned *)(tile + r * TROW + 8 * c);
+      d[0] = v.x;
+      d[1] = v.y;
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t g = 8 * kb + 2 * j + (l >> 5);
-      const unsigned v = (row < bl.rows && g < bl.groups) ? scales[row * bl.groups + g] : 127u;
-      w |= v << (8 * j);
+      for (int i = 0; i < 8; ++i) {
+        const int64_t g = g0 + i;
+        tile[r * TROW + 8 * c + i] = (row < bl.rows && g < bl.groups) ? scales[row * bl.groups + g] : (uint8_t)127;
+      }
     }
-    out[d] = w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int w = t + k * BT, b = w >> 6, l = w & 63;
+    if (kb0 + b >= bl.gblocks) continue;
+    const uint8_t *src = tile + (l & 31) * TROW + 8 * b + (l >> 5);
+    const unsigned word = (unsigned)src[0] | ((unsigned)src[2] << 8) | ((unsigned)src[4] << 16) | ((unsigned)src[6] << 24);
+    out[(rb * bl.gblocks + kb0 + b) * 64 + l] = word;
   }
 }
 
 hipError_t launch_scales_to_blocked(const uint8_t *scales, const BlockedScales &bl, uint8_t *out,
                                     hipStream_t stream) {
-  const int64_t n_words = ((bl.rows + 31) / 32) * bl.gblocks * 64;
-  int64_t g = (n_words + BT - 1) / BT;
-  if (g > (1 << 20)) g = 1 << 20;
-  k_scales_to_blocked<<<(unsigned)g, BT, 0, stream>>>(scales, bl, (unsigned *)out, n_words);
+  const dim3 grid((unsigned)((bl.rows + 31) / 32), (unsigned)((bl.gblocks + SPAN - 1) / SPAN));
+  k_scales_to_blocked<<<grid, BT, 0, stream>>>(scales, bl, (unsigned *)out);
   return hipGetLastError();
 }
 
