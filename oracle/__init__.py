@@ -88,6 +88,19 @@ def lib():
         L.orc_blocked_size.restype = i64
         L.orc_scales_to_blocked.argtypes = [vp, i64, i64, vp]
         L.orc_scales_to_blocked.restype = i32
+        f32 = ctypes.c_float
+        L.orc_nv_scale_byte_n.argtypes = [f32, vp, i64, vp]
+        L.orc_nv_scale_byte_n.restype = None
+        L.orc_nv_code_n.argtypes = [f32, vp, vp, i64, vp]
+        L.orc_nv_code_n.restype = None
+        L.orc_nv_value_n.argtypes = [f32, vp, vp, i64, vp]
+        L.orc_nv_value_n.restype = None
+        L.orc_nv_quantize.argtypes = [vp, i64, i64, vp, i32, f32, vp, vp]
+        L.orc_nv_quantize.restype = i32
+        L.orc_nv_qdq.argtypes = [vp, i64, i64, vp, i32, f32, vp]
+        L.orc_nv_qdq.restype = i32
+        L.orc_nv_dequantize.argtypes = [vp, vp, i64, i64, f32, i32, vp]
+        L.orc_nv_dequantize.restype = i32
         _lib = L
     return _lib
 
@@ -300,3 +313,80 @@ def scales_to_blocked(scales: np.ndarray, K: int) -> np.ndarray:
     if lib().orc_scales_to_blocked(scales.ctypes.data, M, K, out.ctypes.data) != 0:
         raise ValueError("oracle rejected the arguments")
     return out
+
+
+# ---- NVFP4 (a reading; steps in mxoracle.h) -----------------------------------
+
+def nv_scale_byte_n(g: float, amax: np.ndarray) -> np.ndarray:
+    amax = np.ascontiguousarray(amax, dtype=np.float32)
+    out = np.empty(amax.shape, dtype=np.uint8)
+    lib().orc_nv_scale_byte_n(float(np.float32(g)), amax.ctypes.data, amax.size, out.ctypes.data)
+    return out
+
+
+def nv_code_n(g: float, sb: np.ndarray, x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    sb = np.ascontiguousarray(np.broadcast_to(sb, x.shape), dtype=np.uint8)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().orc_nv_code_n(float(np.float32(g)), sb.ctypes.data, x.ctypes.data, x.size, out.ctypes.data)
+    return out
+
+
+def nv_value_n(g: float, sb: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    sb = np.ascontiguousarray(np.broadcast_to(sb, codes.shape), dtype=np.uint8)
+    out = np.empty(codes.shape, dtype=np.float32)
+    lib().orc_nv_value_n(float(np.float32(g)), sb.ctypes.data, codes.ctypes.data, codes.size, out.ctypes.data)
+    return out
+
+
+def nv_quantize(src: np.ndarray, g: float, rot=None, rot_size: int = 0, threads: int = 1):
+    """NVFP4 quantize of bf16 bits [M, K] -> (codes [M, K/2], E4M3 scale bytes [M, K/16])."""
+    src = np.ascontiguousarray(src, dtype=np.uint16)
+    M, K = src.shape
+    codes = np.empty((M, K // 2), dtype=np.uint8)
+    scales = np.empty((M, K // 16), dtype=np.uint8)
+    rp = None if rot is None else np.ascontiguousarray(rot, dtype=np.uint16)
+
+    def run(r0, r1):
+        rc = lib().orc_nv_quantize(src[r0:].ctypes.data, r1 - r0, K, None if rp is None else rp.ctypes.data,
+                                   rot_size, float(np.float32(g)), codes[r0:].ctypes.data, scales[r0:].ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+
+    _run_rows(run, M, threads)
+    return codes, scales
+
+
+def nv_qdq(src: np.ndarray, g: float, rot=None, rot_size: int = 0, threads: int = 1) -> np.ndarray:
+    """NVFP4 quantize-dequantize of bf16 bits [M, K] -> bf16 bits."""
+    src = np.ascontiguousarray(src, dtype=np.uint16)
+    M, K = src.shape
+    dst = np.empty((M, K), dtype=np.uint16)
+    rp = None if rot is None else np.ascontiguousarray(rot, dtype=np.uint16)
+
+    def run(r0, r1):
+        rc = lib().orc_nv_qdq(src[r0:].ctypes.data, r1 - r0, K, None if rp is None else rp.ctypes.data,
+                              rot_size, float(np.float32(g)), dst[r0:].ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+
+    _run_rows(run, M, threads)
+    return dst
+
+
+def nv_dequantize(codes: np.ndarray, scales: np.ndarray, K: int, g: float, dst_dtype: int = BF16,
+                  threads: int = 1) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    M = scales.shape[0]
+    dst = np.empty((M, K), dtype=np.uint16 if dst_dtype == BF16 else np.uint32)
+
+    def run(r0, r1):
+        rc = lib().orc_nv_dequantize(codes[r0:].ctypes.data, scales[r0:].ctypes.data, r1 - r0, K,
+                                     float(np.float32(g)), dst_dtype, dst[r0:].ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+
+    _run_rows(run, M, threads)
+    return dst

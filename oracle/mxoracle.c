@@ -475,3 +475,161 @@ int orc_scales_to_blocked(const uint8_t *scales, int64_t M, int64_t K,
     }
     return 0;
 }
+
+/* ---- NVFP4 (a reading; the steps are listed in mxoracle.h) ------------- */
+
+int orc_nv_scale_byte(float g, float amax)
+{
+    float c6 = g / 6.0f;
+    float q = amax * c6;
+    return orc_encode(ORC_E4M3, (double)q, 0); /* q >= 0; saturates at 448 */
+}
+
+int orc_nv_code(float g, int sb, float x)
+{
+    float sbv = (float)orc_decode(ORC_E4M3, sb);
+    float m = (sbv == 0.0f) ? 0.0f : g / sbv;
+    float v = x * m;
+    return orc_encode(ORC_E2M1, (double)v, 0);
+}
+
+float orc_nv_value(float g, int sb, int code)
+{
+    float sbv = (float)orc_decode(ORC_E4M3, sb);
+    float k = sbv / g;
+    float cv = (float)orc_decode(ORC_E2M1, code);
+    return cv * k;
+}
+
+void orc_nv_scale_byte_n(float g, const float *amax, int64_t n, uint8_t *sb)
+{
+    for (int64_t i = 0; i < n; ++i)
+        sb[i] = (uint8_t)orc_nv_scale_byte(g, amax[i]);
+}
+
+void orc_nv_code_n(float g, const uint8_t *sb, const float *x, int64_t n,
+                   uint8_t *codes)
+{
+    for (int64_t i = 0; i < n; ++i)
+        codes[i] = (uint8_t)orc_nv_code(g, sb[i], x[i]);
+}
+
+void orc_nv_value_n(float g, const uint8_t *sb, const uint8_t *codes,
+                    int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_nv_value(g, sb[i], codes[i]);
+}
+
+static int nv_valid_shape(int64_t M, int64_t K, int rot_size, const void *rot)
+{
+    if (M < 0 || K < 0 || K % 16 != 0)
+        return 0;
+    if (rot_size == 0)
+        return 1;
+    if (rot_size != 16 && rot_size != 32 && rot_size != 64 && rot_size != 128)
+        return 0;
+    return rot != NULL && K % rot_size == 0 && K % 32 == 0;
+}
+
+/* One row of NVFP4: codes (one per element) and scale bytes (one per
+ * 16-group) of the fp32 values x (the source, or its rotation rounded once
+ * to fp32). */
+static void nv_row(float g, const float *x, int64_t K, int *codes,
+                   uint8_t *scales)
+{
+    for (int64_t c = 0; c < K; c += 16) {
+        float amax = 0.0f;
+        for (int j = 0; j < 16; ++j)
+            if (fabsf(x[c + j]) > amax)
+                amax = fabsf(x[c + j]);
+        int sb = orc_nv_scale_byte(g, amax);
+        scales[c / 16] = (uint8_t)sb;
+        for (int j = 0; j < 16; ++j)
+            codes[c + j] = orc_nv_code(g, sb, x[c + j]);
+    }
+}
+
+static void nv_row_values(const void *src, int64_t i, int64_t K,
+                          const double *R, int r, double *x, double *y,
+                          double *beta, float *xf)
+{
+    rotate_row(src, ORC_BF16, i, K, R, r, x, y, beta);
+    for (int64_t k = 0; k < K; ++k)
+        xf[k] = (float)y[k]; /* exact without rotation; one rounding with */
+}
+
+int orc_nv_quantize(const void *src, int64_t M, int64_t K, const void *rot,
+                    int rot_size, float g, uint8_t *codes, uint8_t *scales)
+{
+    if (!nv_valid_shape(M, K, rot_size, rot))
+        return -1;
+    double *R = load_rot(rot, ORC_BF16, rot_size);
+    size_t kk = (size_t)(K ? K : 1);
+    double *x = (double *)malloc(sizeof(double) * kk);
+    double *y = (double *)malloc(sizeof(double) * kk);
+    double *beta = (double *)malloc(sizeof(double) * kk);
+    float *xf = (float *)malloc(sizeof(float) * kk);
+    int *rc = (int *)malloc(sizeof(int) * kk);
+    for (int64_t i = 0; i < M; ++i) {
+        nv_row_values(src, i, K, R, rot_size, x, y, beta, xf);
+        nv_row(g, xf, K, rc, scales + i * (K / 16));
+        for (int64_t col = 0; col < K; col += 2)
+            codes[(i * K + col) / 2] =
+                (uint8_t)((rc[col] & 0xF) | ((rc[col + 1] & 0xF) << 4));
+    }
+    free(x);
+    free(y);
+    free(beta);
+    free(xf);
+    free(rc);
+    free(R);
+    return 0;
+}
+
+int orc_nv_qdq(const void *src, int64_t M, int64_t K, const void *rot,
+               int rot_size, float g, uint16_t *dst)
+{
+    if (!nv_valid_shape(M, K, rot_size, rot))
+        return -1;
+    double *R = load_rot(rot, ORC_BF16, rot_size);
+    size_t kk = (size_t)(K ? K : 1);
+    double *x = (double *)malloc(sizeof(double) * kk);
+    double *y = (double *)malloc(sizeof(double) * kk);
+    double *beta = (double *)malloc(sizeof(double) * kk);
+    float *xf = (float *)malloc(sizeof(float) * kk);
+    int *rc = (int *)malloc(sizeof(int) * kk);
+    uint8_t *sc = (uint8_t *)malloc(kk / 16 + 1);
+    for (int64_t i = 0; i < M; ++i) {
+        nv_row_values(src, i, K, R, rot_size, x, y, beta, xf);
+        nv_row(g, xf, K, rc, sc);
+        for (int64_t col = 0; col < K; ++col)
+            dst[i * K + col] = orc_bf16_from_double(
+                (double)orc_nv_value(g, sc[col / 16], rc[col]));
+    }
+    free(x);
+    free(y);
+    free(beta);
+    free(xf);
+    free(rc);
+    free(sc);
+    free(R);
+    return 0;
+}
+
+int orc_nv_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t M,
+                      int64_t K, float g, int dst_dtype, void *dst)
+{
+    if (!valid_dtype(dst_dtype) || !nv_valid_shape(M, K, 0, NULL))
+        return -1;
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t col = 0; col < K; ++col) {
+            int64_t idx = i * K + col;
+            int code = (col % 2 == 0) ? (codes[idx / 2] & 0xF)
+                                      : (codes[idx / 2] >> 4);
+            float v = orc_nv_value(g, scales[idx / 16], code);
+            store_dst(dst, dst_dtype, idx, (double)v);
+        }
+    }
+    return 0;
+}

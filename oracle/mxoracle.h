@@ -131,6 +131,44 @@ int64_t orc_blocked_size(int64_t M, int64_t K);
 int orc_scales_to_blocked(const uint8_t *scales, int64_t M, int64_t K,
                           uint8_t *out);
 
+/* NVFP4 (a reading).  The pages name NVFP4 beside MXFP4 with the same fused
+ * rotations and show its call shape -- fusedQuantizeNv(a, rotation,
+ * global_scale), scales viewed as [-1, K/16] ("Add QuTLASS support to
+ * vLLM", Purpose: NVFP4 and MXFP4; review of
+ * benchmarks/kernels/bench_nvfp4_qutlass.py) -- but no rule.  Reading, the
+ * published two-level NVFP4 format: groups of 16 elements along K, an E4M3
+ * block scale per group, E2M1 elements, and a per-tensor fp32 multiplier g
+ * (global_scale, g > 0, finite) applied before the block scale.  Because
+ * floating point decides the codes, the steps are fixed as IEEE fp32
+ * operations, each rounded to nearest-even:
+ *   c6   = g / 6                      (per tensor)
+ *   q    = amax * c6                  (amax = max |x| over the group)
+ *   sb   = E4M3(q)                    (nearest-even, saturating at 448;
+ *                                      the scale byte; q <= 2^-10 gives 0)
+ *   m    = g / value(sb)              (0 when value(sb) = 0)
+ *   code = E2M1(x * m)                (nearest-even, saturating at 6, sign
+ *                                      kept)
+ *   deq  = value(code) * (value(sb) / g), then nearest-even to bf16.
+ * x is the bf16 source, or (with a rotation) the rotated value rounded once
+ * to fp32.  Non-finite input is outside the contract. */
+int orc_nv_scale_byte(float g, float amax);
+int orc_nv_code(float g, int sb, float x);
+float orc_nv_value(float g, int sb, int code);
+void orc_nv_scale_byte_n(float g, const float *amax, int64_t n, uint8_t *sb);
+void orc_nv_code_n(float g, const uint8_t *sb, const float *x, int64_t n,
+                   uint8_t *codes);
+void orc_nv_value_n(float g, const uint8_t *sb, const uint8_t *codes,
+                    int64_t n, float *out);
+/* Whole matrices: bf16 source [M x K], K % 16 == 0 (with a rotation also
+ * K % r == 0 and K % 32 == 0); codes [M x K/2] (even column in bits 3:0),
+ * E4M3 scale bytes [M x K/16] row-major; QDQ output bf16. */
+int orc_nv_quantize(const void *src, int64_t M, int64_t K, const void *rot,
+                    int rot_size, float g, uint8_t *codes, uint8_t *scales);
+int orc_nv_qdq(const void *src, int64_t M, int64_t K, const void *rot,
+               int rot_size, float g, uint16_t *dst);
+int orc_nv_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t M,
+                      int64_t K, float g, int dst_dtype, void *dst);
+
 #ifdef __cplusplus
 }
 #endif

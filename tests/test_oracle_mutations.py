@@ -24,6 +24,11 @@ MUTANTS = {
     "blocked_lane_from_group_pair": ("int64_t lane = 32 * (g % 2) + i % 32;",
                                      "int64_t lane = 32 * ((g % 8) / 4) + i % 32;"),
     "blocked_byte_order": ("int64_t byte = (g % 8) / 2;", "int64_t byte = 3 - (g % 8) / 2;"),
+    "nvfp4_c6_inverted": ("float c6 = g / 6.0f;", "float c6 = 6.0f / g;"),
+    "nvfp4_scale_order": ("float q = amax * c6;", "float q = (amax * g) / 6.0f;"),
+    "nvfp4_element_order": ("float v = x * m;", "float v = (sbv == 0.0f) ? 0.0f : (x * g) / sbv;"),
+    "nvfp4_dequant_inverted": ("float k = sbv / g;", "float k = g / sbv;"),
+    "nvfp4_amax_first_only": ("if (fabsf(x[c + j]) > amax)", "if (j == 0)"),
     "exact_dequant_scale_bias": ("dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 127);",
                                  "dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 128);"),
     "exact_dequant_sign_dropped": ("dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 127);",

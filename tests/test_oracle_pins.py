@@ -569,3 +569,132 @@ def test_blocked_size_rejects_bad_shapes(orc):
     assert orc.blocked_size(4, 48) == -1
     assert orc.blocked_size(-1, 32) == -1
     assert orc.blocked_size(0, 32) == 0
+
+
+# ---- NVFP4 (reading) ----------------------------------------------------------
+
+NVGOLD = os.path.join(os.path.dirname(__file__), "golden", "nvfp4_groups.json")
+
+
+def _num(v):
+    return -0.0 if v == "-0.0" else float(v)
+
+
+@pytest.mark.parametrize("grp", json.load(open(NVGOLD))["groups"], ids=lambda g: g["name"])
+def test_nvfp4_hand_worked_group(orc, grp):
+    x = np.zeros(16, dtype=np.float32)
+    x[:len(grp["x"])] = [_num(v) for v in grp["x"]]
+    bits = W.f32_to_bf16_bits(x)[None]
+    assert np.array_equal(W.bf16_bits_to_f32(bits)[0], x)  # the inputs are bf16 values
+    codes, scales = orc.nv_quantize(bits, grp["g"])
+    assert int(scales[0, 0]) == grp["scale"]
+    got = np.stack([codes[0] & 0xF, codes[0] >> 4], 1).ravel()
+    want = np.zeros(16, dtype=np.uint8)
+    want[:len(grp["codes"])] = grp["codes"]
+    if grp["name"] == "N2":
+        want[:] = 0
+    assert np.array_equal(got, want)
+    deq = W.bf16_bits_to_f32(orc.nv_qdq(bits, grp["g"]))[0].astype(np.float64)
+    wd = np.zeros(16)
+    wd[:len(grp["deq"])] = [_num(v) for v in grp["deq"]]
+    assert np.array_equal(deq, wd) and np.array_equal(np.signbit(deq), np.signbit(wd))
+
+
+def test_nvfp4_power_of_two_closed_form(orc):
+    # g = 6 * 2^k and amax = 2^e: c6 = 2^k, q = 2^(e+k), m = 6 * 2^-e exactly,
+    # so the codes are the nearest-even E2M1 values of 6 x / 2^e
+    rng = np.random.default_rng(21)
+    for k, e in [(0, 0), (-3, 2), (4, -5), (2, 3), (-6, -1)]:
+        x = (rng.standard_normal((64, 16)) * 2.0 ** (e - 1)).astype(np.float32)
+        x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x))
+        x = np.clip(x, -(2.0 ** e) * 0.999, 2.0 ** e * 0.999)
+        x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x.astype(np.float32)))
+        x[:, 0] = 2.0 ** e  # the group maximum
+        codes, scales = orc.nv_quantize(W.f32_to_bf16_bits(x), 6.0 * 2.0 ** k)
+        assert (scales == brute_force_codes(E4M3, np.full(scales.shape, 2.0 ** (e + k)), 0)).all()
+        got = np.stack([codes & 0xF, codes >> 4], -1).reshape(64, 16)
+        assert np.array_equal(got, brute_force_codes(E2M1, 6.0 * x.astype(np.float64) / 2.0 ** e, 0))
+
+
+def _nv_numpy(x32, g):
+    """The fp32 steps with numpy float32 arithmetic and brute-force rounding."""
+    g = np.float32(g)
+    c6 = g / np.float32(6)
+    amax = np.abs(x32).max(-1)
+    q = (amax * c6).astype(np.float32)
+    sb = brute_force_codes(E4M3, q.astype(np.float64), 0)
+    sbv = textbook_grid(E4M3)[sb].astype(np.float32)
+    with np.errstate(divide="ignore"):
+        m = np.where(sbv == 0, np.float32(0), g / sbv).astype(np.float32)
+    v = (x32 * m[..., None]).astype(np.float32)
+    codes = brute_force_codes(E2M1, v.astype(np.float64), 0)
+    k = (sbv / g).astype(np.float32)
+    cv = textbook_grid(E2M1)[codes & 7] * np.where(codes & 8, -1.0, 1.0)
+    deq = (cv.astype(np.float32) * k[..., None]).astype(np.float32)
+    return sb, codes, deq
+
+
+def test_nvfp4_matches_numpy_float32_steps(orc):
+    rng = np.random.default_rng(22)
+    M, K = 96, 256
+    x = rng.standard_t(3, (M, K)) * np.exp2(rng.integers(-12, 12, (M, 1)))
+    bits = W.f32_to_bf16_bits(x.astype(np.float32))
+    x32 = W.bf16_bits_to_f32(bits)
+    for g in (1.0, 448.0 * 6.0 / float(np.abs(x32).max()), 0.37, 3.0e4):
+        codes, scales = orc.nv_quantize(bits, g, threads=4)
+        sb, wc, deq = _nv_numpy(x32.reshape(M, K // 16, 16), g)
+        assert np.array_equal(scales, sb.reshape(M, K // 16))
+        got = np.stack([codes & 0xF, codes >> 4], -1).reshape(M, K)
+        assert np.array_equal(got, wc.reshape(M, K))
+        qdq = orc.nv_qdq(bits, g, threads=4)
+        assert np.array_equal(qdq, W.f32_to_bf16_bits(deq.reshape(M, K)))
+        dq32 = orc.nv_dequantize(codes, scales, K, g, dst_dtype=1).view(np.float32)
+        assert np.array_equal(dq32.view(np.uint32), deq.reshape(M, K).view(np.uint32))
+
+
+def test_nvfp4_operation_order_is_pinned(orc):
+    """Inputs where x*(g/sbv) and (x*g)/sbv, or amax*(g/6) and (amax*g)/6,
+    round to different codes (found by aiming g at a rounding midpoint): the
+    oracle follows the stated order."""
+    rng = np.random.default_rng(23)
+    grid4, grid8 = textbook_grid(E2M1), textbook_grid(E4M3)
+    mids4 = (grid4[1:] + grid4[:-1]) / 2
+    mids8 = (grid8[1:] + grid8[:-1]) / 2
+
+    def bf16(v):
+        return np.float32(W.bf16_bits_to_f32(W.f32_to_bf16_bits(np.array([v], np.float32)))[0])
+
+    found_m, found_q = [], []
+    for _ in range(3000):
+        x = bf16(rng.uniform(0.01, 50.0))
+        sbv = np.float32(grid8[rng.integers(30, 120)])
+        mid = rng.choice(mids4)
+        g0 = np.float32(mid * float(sbv) / float(x))
+        for g in (g0, np.nextafter(g0, np.float32(0)), np.nextafter(g0, np.float32(np.inf))):
+            a = brute_force_codes(E2M1, np.array([float(np.float32(x * np.float32(g / sbv)))]), 0)[0]
+            b = brute_force_codes(E2M1, np.array([float(np.float32(np.float32(x * g) / sbv))]), 0)[0]
+            if a != b:
+                found_m.append((float(g), int(brute_force_codes(E4M3, np.array([float(sbv)]), 0)[0]), float(x), int(a)))
+        amax = bf16(rng.uniform(0.01, 100.0))
+        mid = rng.choice(mids8[:126])
+        g0 = np.float32(mid * 6.0 / float(amax))
+        for g in (g0, np.nextafter(g0, np.float32(0)), np.nextafter(g0, np.float32(np.inf))):
+            qa = np.float32(amax * np.float32(g / np.float32(6)))
+            qb = np.float32(np.float32(amax * g) / np.float32(6))
+            ca = brute_force_codes(E4M3, np.array([float(qa)]), 0)[0]
+            cb = brute_force_codes(E4M3, np.array([float(qb)]), 0)[0]
+            if ca != cb:
+                found_q.append((float(g), float(amax), int(ca)))
+    assert len(found_m) >= 5 and len(found_q) >= 5, (len(found_m), len(found_q))
+    for g, sb, x, a in found_m[:50]:
+        assert orc.nv_code_n(g, np.array([sb], np.uint8), np.array([x], np.float32))[0] == a
+    for g, amax, ca in found_q[:50]:
+        assert orc.nv_scale_byte_n(g, np.array([amax], np.float32))[0] == ca
+
+
+def test_nvfp4_rejects_bad_shapes(orc):
+    bits = np.zeros((2, 24), np.uint16)
+    with pytest.raises(ValueError):
+        orc.nv_quantize(bits, 1.0)
+    with pytest.raises(ValueError):
+        orc.nv_quantize(np.zeros((2, 48), np.uint16), 1.0, rot=np.zeros((16, 16), np.uint16), rot_size=16)
