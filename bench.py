@@ -234,6 +234,24 @@ def main():
                        "GBps": round(4 * n / (avg * 1e-3) / 1e9, 1),
                        "frac_of_peak": round(4 * n / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)})
     del deq_out
+    # NVFP4 (16-groups, E4M3 scales, per-tensor multiplier 448*6/amax) on the
+    # same layer: QDQ and quantize, without rotation and with rotation 128
+    gsc = (448.0 * 6.0 / x.abs().max().float()).reshape(1).contiguous()
+    nv_scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    for op, r in (("qdq", 0), ("qdq", 128), ("quantize", 0), ("quantize", 128)):
+        R = rots[r][1] if r else None
+        if op == "qdq":
+            fn = (lambda R=R: mx.mx_nvfp4_qdq(x, gsc, rot=R, dst=dst))
+            bts = 4.0 * n
+        else:
+            fn = (lambda R=R: mx.mx_nvfp4_quantize(x, gsc, rot=R, codes=codes[0], scales=nv_scales))
+            bts = n * (2.0 + 0.5 + 1.0 / 16.0)
+        fn()
+        avg, mn = timed(fn, 10)
+        extras.append({"kernel": f"nvfp4_{op}_rot{r}", "bytes": int(bts), "avg_us": round(avg * 1e3, 2),
+                       "min_us": round(mn * 1e3, 2), "GBps": round(bts / (avg * 1e-3) / 1e9, 1),
+                       "frac_of_peak": round(bts / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)})
+    del nv_scales
     # blocked scale layout: the step's quantize with blocked scales, and the
     # re-blocking of row-major scales
     blk = torch.empty(mx.mx_blocked_scales_bytes(M, K), dtype=torch.uint8, device=dev)

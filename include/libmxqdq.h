@@ -75,9 +75,11 @@ extern "C" {
 #define MX_OK 0
 #define MX_EFMT (-1)    /* fmt is not MX_FMT_E2M1 / MX_FMT_E4M3            */
 #define MX_EDTYPE (-2)  /* dtype is not MX_DTYPE_BF16 / MX_DTYPE_F32        */
-#define MX_ESHAPE (-3)  /* M < 0, K < 0, K % 32 != 0, or M*K too large      */
+#define MX_ESHAPE (-3)  /* M < 0, K < 0, K % 32 != 0 (NVFP4: K % 16), or
+                           M*K too large                                    */
 #define MX_EROT (-4)    /* rot_size not in {0,16,32,64,128}, K % rot_size,
-                           or rot == NULL with rot_size > 0                  */
+                           rot == NULL with rot_size > 0, or (NVFP4)
+                           a rotation with K % 32 != 0                       */
 #define MX_ENULL (-5)   /* a required pointer is NULL                       */
 #define MX_EALIGN (-6)  /* a pointer breaks the alignment stated above      */
 #define MX_ELAUNCH (-7) /* the kernel launch failed (hipGetLastError)       */
@@ -185,6 +187,43 @@ MX_API int mx_matmul(int fmt, const uint8_t *a_codes, const uint8_t *a_scales,
                      const uint8_t *b_codes, const uint8_t *b_scales,
                      int scale_layout, int64_t M, int64_t N, int64_t K,
                      float alpha, int out_dtype, void *c);
+
+/*
+ * NVFP4: the second 4-bit format the pages name beside MXFP4, with the same
+ * fused rotations ("Add QuTLASS support to vLLM", Purpose: NVFP4 and MXFP4;
+ * review of benchmarks/kernels/bench_nvfp4_qutlass.py: fusedQuantizeNv(a,
+ * rotation, global_scale), scales viewed as [-1, K/16]).  The pages give no
+ * rule; the reading is the published two-level NVFP4 format: groups of 16
+ * elements along K, one E4M3 block scale per group, E2M1 elements, and a
+ * per-tensor fp32 multiplier g = *global_scale (positive and finite; e.g.
+ * 448 * 6 / amax of the tensor).  The steps are fp32 operations, each
+ * rounded to nearest-even, so that the codes are defined exactly:
+ *   c6 = g / 6;  q = amax * c6 (amax: the group's abs-max);
+ *   scale byte = E4M3(q), nearest-even, saturating at 448 (0x7E); q <= 2^-10
+ *   gives 0;  m = g / value(scale), or 0 for a zero scale;
+ *   code = E2M1(x * m), nearest-even, saturating at 6, sign kept;
+ *   dequantized value = value(code) * (value(scale) / g), then nearest-even
+ *   into the destination type.
+ * With a rotation, x is the rotated value (fp32 accumulation), as for MX.
+ *   src          [M x K] bf16, K % 16 == 0 (with a rotation also K % r == 0
+ *                and K % 32 == 0), 16-byte aligned.
+ *   codes        [M x K/2] bytes, column 2k in bits 3:0; 16-byte aligned.
+ *   scales       [M x K/16] E4M3 bytes, row-major; 4-byte aligned.
+ *   global_scale device pointer to one fp32, 4-byte aligned; read by the
+ *                kernel (so it may be computed on the device).
+ * Non-finite input, or g not positive and finite, is outside the contract.
+ */
+MX_API int mx_nvfp4_quantize(const void *src, int64_t M, int64_t K,
+                             const void *rot, int rot_size,
+                             const float *global_scale, uint8_t *codes,
+                             uint8_t *scales);
+MX_API int mx_nvfp4_qdq(const void *src, int64_t M, int64_t K,
+                        const void *rot, int rot_size,
+                        const float *global_scale, void *dst);
+MX_API int mx_nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales,
+                               int64_t M, int64_t K,
+                               const float *global_scale, int dst_dtype,
+                               void *dst);
 
 /* Stream used by the calling thread's subsequent calls (a hipStream_t;
  * NULL = the default stream).  The setting is thread-local. */

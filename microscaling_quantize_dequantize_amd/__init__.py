@@ -8,6 +8,7 @@ entry-point names.  The binding is loaded on first use so that importing
 
 __all__ = ["mx_qdq", "mx_quantize", "mx_dequantize", "mx_rotate", "mx_matmul",
            "mx_blocked_scales_bytes", "mx_scales_to_blocked", "mx_quantize_blocked",
+           "mx_nvfp4_quantize", "mx_nvfp4_qdq", "mx_nvfp4_dequantize",
            "mx_set_stream", "mx_status_string", "MXError",
            "E2M1", "E4M3", "BF16", "F32", "ROWMAJOR", "BLOCKED"]
 

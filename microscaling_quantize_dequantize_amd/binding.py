@@ -40,12 +40,16 @@ _lib.mx_blocked_scales_bytes.argtypes = [_i64, _i64]
 _lib.mx_blocked_scales_bytes.restype = _i64
 _lib.mx_scales_to_blocked.argtypes = [_vp, _i64, _i64, _vp]
 _lib.mx_quantize_blocked.argtypes = [_int, _vp, _i64, _i64, _vp, _int, _vp, _vp]
+_lib.mx_nvfp4_quantize.argtypes = [_vp, _i64, _i64, _vp, _int, _vp, _vp, _vp]
+_lib.mx_nvfp4_qdq.argtypes = [_vp, _i64, _i64, _vp, _int, _vp, _vp]
+_lib.mx_nvfp4_dequantize.argtypes = [_vp, _vp, _i64, _i64, _vp, _int, _vp]
 _lib.mx_set_stream.argtypes = [_vp]
 _lib.mx_get_stream.restype = _vp
 _lib.mx_status_string.argtypes = [_int]
 _lib.mx_status_string.restype = ctypes.c_char_p
 for _f in (_lib.mx_qdq, _lib.mx_quantize, _lib.mx_dequantize, _lib.mx_rotate, _lib.mx_matmul,
-           _lib.mx_scales_to_blocked, _lib.mx_quantize_blocked):
+           _lib.mx_scales_to_blocked, _lib.mx_quantize_blocked, _lib.mx_nvfp4_quantize, _lib.mx_nvfp4_qdq,
+           _lib.mx_nvfp4_dequantize):
     _f.restype = _int
 
 
@@ -201,6 +205,57 @@ def mx_matmul(fmt: int, a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: 
                          _dev(b_scales, "b_scales"), scale_layout, M, N, K, float(alpha), _DTYPE[c.dtype],
                          _dev(c, "c")))
     return c
+
+
+def _gscale(global_scale: torch.Tensor) -> int:
+    if global_scale.dtype != torch.float32 or global_scale.numel() != 1:
+        raise ValueError("global_scale must be a one-element float32 tensor")
+    return _dev(global_scale, "global_scale")
+
+
+def mx_nvfp4_quantize(src: torch.Tensor, global_scale: torch.Tensor, rot: torch.Tensor | None = None,
+                      codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """NVFP4 quantize of bf16 src [M, K] -> (E2M1 codes [M, K/2], E4M3 scale bytes [M, K/16])."""
+    M, K = _mk(src)
+    if src.dtype != torch.bfloat16:
+        raise TypeError("mx_nvfp4_quantize takes bfloat16 input")
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty((M, K // 16), dtype=torch.uint8, device=src.device)
+    rp, r = _rot(rot, src.dtype)
+    _stream()
+    _call(_lib.mx_nvfp4_quantize(_dev(src, "src"), M, K, rp, r, _gscale(global_scale), _dev(codes, "codes"),
+                                 _dev(scales, "scales")))
+    return codes, scales
+
+
+def mx_nvfp4_qdq(src: torch.Tensor, global_scale: torch.Tensor, rot: torch.Tensor | None = None,
+                 dst: torch.Tensor | None = None) -> torch.Tensor:
+    """NVFP4 quantize-dequantize of bf16 src [M, K] into bf16 dst."""
+    M, K = _mk(src)
+    if src.dtype != torch.bfloat16:
+        raise TypeError("mx_nvfp4_qdq takes bfloat16 input")
+    if dst is None:
+        dst = torch.empty_like(src)
+    if dst.dtype != src.dtype or dst.shape != src.shape:
+        raise ValueError("dst must match src in dtype and shape")
+    rp, r = _rot(rot, src.dtype)
+    _stream()
+    _call(_lib.mx_nvfp4_qdq(_dev(src, "src"), M, K, rp, r, _gscale(global_scale), _dev(dst, "dst")))
+    return dst
+
+
+def mx_nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, K: int, global_scale: torch.Tensor,
+                        dtype: torch.dtype = torch.bfloat16, dst: torch.Tensor | None = None):
+    """NVFP4 codes + E4M3 scales -> [M, K] of `dtype`."""
+    M = scales.shape[0]
+    if dst is None:
+        dst = torch.empty((M, K), dtype=dtype, device=codes.device)
+    _stream()
+    _call(_lib.mx_nvfp4_dequantize(_dev(codes, "codes"), _dev(scales, "scales"), M, K, _gscale(global_scale),
+                                   _DTYPE[dst.dtype], _dev(dst, "dst")))
+    return dst
 
 
 def raw():

@@ -163,6 +163,56 @@ MX_API int mx_matmul(int fmt, const uint8_t *a_codes, const uint8_t *a_scales, c
                                   out_dtype, c, tl_stream));
 }
 
+namespace {
+
+int check_nv(int64_t M, int64_t K, const void *rot, int r) {
+  if (M < 0 || K < 0 || K % 16 != 0) return MX_ESHAPE;
+  if (K > 0 && M > MAX_ELEMS / K) return MX_ESHAPE;
+  if (r != 0 && K % 32 != 0) return MX_EROT;  // rotation blocks hold whole 32-element tiles
+  return check_rot(rot, r, K, true);
+}
+
+}  // namespace
+
+MX_API int mx_nvfp4_quantize(const void *src, int64_t M, int64_t K, const void *rot, int rot_size,
+                             const float *global_scale, uint8_t *codes, uint8_t *scales) {
+  int st;
+  if ((st = check_nv(M, K, rot, rot_size))) return st;
+  if (M == 0 || K == 0) return MX_OK;
+  if (!src || !global_scale || !codes || !scales) return MX_ENULL;
+  if (!aligned(src, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(global_scale, 4) ||
+      (rot_size && !aligned(rot, 16)))
+    return MX_EALIGN;
+  if (rot_size == 0)
+    return launched(mx::launch_nv_unrot(mx::OP_QUANT, src, nullptr, codes, scales, global_scale, M * K, tl_stream));
+  return launched(mx::launch_nv_rot(mx::OP_QUANT, src, rot, rot_size, nullptr, codes, scales, global_scale, M * K,
+                                    tl_stream));
+}
+
+MX_API int mx_nvfp4_qdq(const void *src, int64_t M, int64_t K, const void *rot, int rot_size,
+                        const float *global_scale, void *dst) {
+  int st;
+  if ((st = check_nv(M, K, rot, rot_size))) return st;
+  if (M == 0 || K == 0) return MX_OK;
+  if (!src || !global_scale || !dst) return MX_ENULL;
+  if (!aligned(src, 16) || !aligned(dst, 16) || !aligned(global_scale, 4) || (rot_size && !aligned(rot, 16)))
+    return MX_EALIGN;
+  if (rot_size == 0)
+    return launched(mx::launch_nv_unrot(mx::OP_QDQ, src, dst, nullptr, nullptr, global_scale, M * K, tl_stream));
+  return launched(mx::launch_nv_rot(mx::OP_QDQ, src, rot, rot_size, dst, nullptr, nullptr, global_scale, M * K,
+                                    tl_stream));
+}
+
+MX_API int mx_nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t M, int64_t K,
+                               const float *global_scale, int dst_dtype, void *dst) {
+  int st;
+  if ((st = check_dtype(dst_dtype)) || (st = check_nv(M, K, nullptr, 0))) return st;
+  if (M == 0 || K == 0) return MX_OK;
+  if (!codes || !scales || !global_scale || !dst) return MX_ENULL;
+  if (!aligned(codes, 16) || !aligned(dst, 16) || !aligned(global_scale, 4)) return MX_EALIGN;
+  return launched(mx::launch_nv_dequant(dst_dtype, codes, scales, global_scale, dst, M * K, tl_stream));
+}
+
 MX_API void mx_set_stream(void *stream) { tl_stream = (hipStream_t)stream; }
 
 MX_API void *mx_get_stream(void) { return (void *)tl_stream; }

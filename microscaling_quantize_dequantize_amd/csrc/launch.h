@@ -26,6 +26,14 @@ hipError_t launch_rot(int fmt, int op, int dtype, const void *src, const void *r
                       void *dst, uint8_t *codes, uint8_t *scales, int64_t n, hipStream_t stream,
                       const BlockedScales *bl = nullptr);
 
+// NVFP4 (g: device pointer to the per-tensor fp32 multiplier; n = M*K).
+hipError_t launch_nv_unrot(int op, const void *src, void *dst, uint8_t *codes, uint8_t *scales, const float *g,
+                           int64_t n, hipStream_t stream);
+hipError_t launch_nv_dequant(int dtype, const uint8_t *codes, const uint8_t *scales, const float *g, void *dst,
+                             int64_t n, hipStream_t stream);
+hipError_t launch_nv_rot(int op, const void *src, const void *rot, int r, void *dst, uint8_t *codes,
+                         uint8_t *scales, const float *g, int64_t n, hipStream_t stream);
+
 hipError_t launch_scales_to_blocked(const uint8_t *scales, const BlockedScales &bl, uint8_t *out,
                                     hipStream_t stream);
 

@@ -186,6 +186,18 @@ __device__ __forceinline__ unsigned bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// ---- NVFP4 scale steps --------------------------------------------------------
+
+// E4M3 scale byte of q >= 0, nearest-even and saturating (the hardware
+// conversion returns NaN past 448, so q is clamped first; 448 is itself a
+// grid value).
+__device__ __forceinline__ unsigned nv_scale_byte(float q) {
+  return fp8_from_f32x2<false>(0u, fminf(q, 448.0f), 0.0f, 1.0f) & 0xFFu;
+}
+
+// fp32 value of a (non-negative) E4M3 scale byte.
+__device__ __forceinline__ float nv_scale_value(unsigned sb) { return decode_mag<1>(sb, 0); }
+
 // ---- blocked scale layout ---------------------------------------------------
 // The operand order of the 32x32x64 scaled MFMA: rows padded to 32, groups
 // to 8; 256-byte blocks of 32 rows x 8 groups in row-major block order; word
@@ -224,6 +236,8 @@ __device__ __forceinline__ void write_blocked_pads(uint8_t *__restrict__ out, co
 enum : int {
   DPP_QUAD_1032 = 0xB1,  // quad_perm [1,0,3,2]
   DPP_QUAD_2301 = 0x4E,  // quad_perm [2,3,0,1]
+  DPP_ROW_SHL2 = 0x102,  // lane i reads lane i+2 of its row (0 past the row's end)
+  DPP_ROW_SHL4 = 0x104,
   DPP_ROW_ROR4 = 0x124,
   DPP_ROW_ROR8 = 0x128,
   DPP_ROW_HALF_MIRROR = 0x141,

@@ -1,0 +1,148 @@
+// NVFP4 quantize / QDQ / dequantize, unrotated (the rotated forms live with
+// the other rotated kernels).
+//
+// The pages name NVFP4 beside MXFP4 ("[Transform] [Quantization] Add QuTLASS
+// support to vLLM", Purpose) and show only its call shape (review of
+// benchmarks/kernels/bench_nvfp4_qutlass.py: fusedQuantizeNv(a, rotation,
+// global_scale), scales viewed as [-1, K/16]).  The steps, as fp32
+// operations rounded to nearest-even (they decide the codes, so they are
+// fixed exactly):
+//   c6 = g / 6 (per tensor);  q = amax * c6;  scale byte = E4M3(q)
+//   (nearest-even, saturating at 448);  m = g / value(scale) (0 for a zero
+//   scale);  code = E2M1(x * m) (nearest-even, saturating, sign kept);
+//   dequantized value = value(code) * (value(scale) / g).
+// Groups are 16 elements, i.e. two 16-byte pieces: a lane pair.
+#include "launch.h"
+#include "mx_device.h"
+
+namespace mx {
+
+namespace {
+
+constexpr int64_t NV_MAX_BLOCKS = (int64_t)1 << 22;
+constexpr int NV_T = 128;
+
+// E2M1 codes of the 8 bf16 values of a piece times m (8 nibbles, element 0
+// in bits 3:0).
+__device__ __forceinline__ unsigned nv_codes(u32x4 w, float m) {
+  const unsigned u[4] = {w.x, w.y, w.z, w.w};
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = __uint_as_float(u[k] << 16) * m;
+    v[2 * k + 1] = __uint_as_float(u[k] & 0xFFFF0000u) * m;
+  }
+  unsigned c = fp4_from_f32x2<0>(0u, v[0], v[1], 1.0f);
+  c = fp4_from_f32x2<1>(c, v[2], v[3], 1.0f);
+  c = fp4_from_f32x2<2>(c, v[4], v[5], 1.0f);
+  return fp4_from_f32x2<3>(c, v[6], v[7], 1.0f);
+}
+
+// Dequantized fp32 value of nibble k of c.
+__device__ __forceinline__ float nv_value(unsigned c, int k, float kf) {
+  return decode_code<0>((c >> (4 * k)) & 0xFu, 0) * kf;
+}
+
+template <int OP>
+__global__ __launch_bounds__(NV_T) void k_nv_unrot(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                                   uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                   const float *__restrict__ gp, int64_t n_pieces) {
+  const float g = *gp;
+  const float c6 = g / 6.0f;
+  const int tid = threadIdx.x;
+  for (int64_t sweep = blockIdx.x; sweep * NV_T < n_pieces; sweep += gridDim.x) {
+    const int64_t p = sweep * NV_T + tid;
+    const u32x4 w = p < n_pieces ? __builtin_nontemporal_load(src + p) : u32x4{0u, 0u, 0u, 0u};
+    // group abs-max: this lane's 8 values, then the other lane of the pair
+    unsigned mb = 0;
+    {
+      u16x2 a = __builtin_bit_cast(u16x2, w.x & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2, w.y & 0x7FFF7FFFu);
+      u16x2 c = __builtin_bit_cast(u16x2, w.z & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2, w.w & 0x7FFF7FFFu);
+      u16x2 mm = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+      mb = umax(mm[0], mm[1]);
+    }
+    mb = umax(mb, dpp<DPP_QUAD_1032>(mb));
+    const float amax = __uint_as_float(mb << 16);
+    const unsigned sb = nv_scale_byte(amax * c6);
+    const float sbv = nv_scale_value(sb);
+    const float m = sbv == 0.0f ? 0.0f : g / sbv;
+    const unsigned c = nv_codes(w, m);
+    if (OP == OP_QDQ) {
+      const float kf = sbv / g;
+      unsigned o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = bf16_rne(nv_value(c, 2 * k, kf)) | (bf16_rne(nv_value(c, 2 * k + 1, kf)) << 16);
+      if (p < n_pieces) __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, dst + p);
+    } else {
+      if (p < n_pieces) __builtin_nontemporal_store(c, (unsigned *)codes + p);
+      // scale bytes: lanes 8k..8k+7 hold 4 consecutive groups; gather the 4
+      // bytes into lane 8k (shifts within the 16-lane row, so that nothing
+      // wraps in from the other half) and store one word per 4 groups
+      unsigned v = sb << (8 * ((tid >> 1) & 3));
+      v |= dpp<DPP_ROW_SHL2>(v);
+      v |= dpp<DPP_ROW_SHL4>(v);
+      if ((tid & 7) == 0 && p < n_pieces) {
+        const int64_t g0 = p >> 1;
+        if (p + 8 <= n_pieces) {
+          *(unsigned *)(scales + g0) = v;
+        } else {
+          for (int k = 0; k < 4; ++k)
+            if (p + 2 * k < n_pieces) scales[g0 + k] = (uint8_t)(v >> (8 * k));
+        }
+      }
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(NV_T) void k_nv_dequant(const uint8_t *__restrict__ codes,
+                                                     const uint8_t *__restrict__ scales,
+                                                     const float *__restrict__ gp, void *__restrict__ dst,
+                                                     int64_t n_pieces) {
+  const float g = *gp;
+  const int64_t stride = (int64_t)gridDim.x * NV_T;
+  for (int64_t p = (int64_t)blockIdx.x * NV_T + threadIdx.x; p < n_pieces; p += stride) {
+    const float kf = nv_scale_value(scales[p >> 1]) / g;
+    const unsigned c = __builtin_nontemporal_load((const unsigned *)codes + p);
+    if (DT == 0) {
+      unsigned o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = bf16_rne(nv_value(c, 2 * k, kf)) | (bf16_rne(nv_value(c, 2 * k + 1, kf)) << 16);
+      __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, (u32x4 *)dst + p);
+    } else {
+      unsigned v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = __float_as_uint(nv_value(c, k, kf));
+      u32x4 *d = (u32x4 *)dst + 2 * p;
+      __builtin_nontemporal_store(u32x4{v[0], v[1], v[2], v[3]}, d);
+      __builtin_nontemporal_store(u32x4{v[4], v[5], v[6], v[7]}, d + 1);
+    }
+  }
+}
+
+unsigned nv_grid(int64_t n_pieces) {
+  const int64_t want = (n_pieces + NV_T - 1) / NV_T;
+  return (unsigned)(want < NV_MAX_BLOCKS ? want : NV_MAX_BLOCKS);
+}
+
+}  // namespace
+
+hipError_t launch_nv_unrot(int op, const void *src, void *dst, uint8_t *codes, uint8_t *scales, const float *g,
+                           int64_t n, hipStream_t stream) {
+  const int64_t np = n / 8;
+  if (op == OP_QDQ)
+    k_nv_unrot<OP_QDQ><<<nv_grid(np), NV_T, 0, stream>>>((const u32x4 *)src, (u32x4 *)dst, nullptr, nullptr, g, np);
+  else
+    k_nv_unrot<OP_QUANT><<<nv_grid(np), NV_T, 0, stream>>>((const u32x4 *)src, nullptr, codes, scales, g, np);
+  return hipGetLastError();
+}
+
+hipError_t launch_nv_dequant(int dtype, const uint8_t *codes, const uint8_t *scales, const float *g, void *dst,
+                             int64_t n, hipStream_t stream) {
+  const int64_t np = n / 8;
+  if (dtype == 0) k_nv_dequant<0><<<nv_grid(np), NV_T, 0, stream>>>(codes, scales, g, dst, np);
+  else k_nv_dequant<1><<<nv_grid(np), NV_T, 0, stream>>>(codes, scales, g, dst, np);
+  return hipGetLastError();
+}
+
+}  // namespace mx

@@ -120,6 +120,47 @@ __device__ __forceinline__ void group_bf16(const unsigned c[4], unsigned sb, flo
   swap_halves(o[5], o[7]);
 }
 
+// NVFP4 on the same 32-wide tile: the tile's outputs j = 0-15 (acc[0..7] of
+// lanes l and l+32) and j = 16-31 (acc[8..15]) are two 16-groups, each with
+// its own E4M3 scale byte (sb[0], sb[1]); the codes come out as for E2M1
+// (c[q]: 4 nibbles of elements 4q..4q+3 of this lane's run).
+__device__ __forceinline__ void nv_group_codes(const f32x16 &acc, float g, float c6, unsigned sb[2],
+                                               float sbv[2], unsigned c[4]) {
+#pragma unroll
+  for (int hg = 0; hg < 2; ++hg) {
+    unsigned m = 0;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) m = umax(m, __float_as_uint(acc[8 * hg + a]) & 0x7FFFFFFFu);
+    m = max_across_halves(m);
+    sb[hg] = nv_scale_byte(__uint_as_float(m) * c6);
+    sbv[hg] = nv_scale_value(sb[hg]);
+  }
+  const float mul[2] = {sbv[0] == 0.0f ? 0.0f : g / sbv[0], sbv[1] == 0.0f ? 0.0f : g / sbv[1]};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float mq = mul[q >> 1];
+    unsigned v = fp4_from_f32x2<0>(0u, acc[4 * q] * mq, acc[4 * q + 1] * mq, 1.0f);
+    c[q] = fp4_from_f32x2<1>(v, acc[4 * q + 2] * mq, acc[4 * q + 3] * mq, 1.0f);
+  }
+}
+
+// Dequantized bf16 of the two 16-groups of a tile, arranged as group_bf16.
+__device__ __forceinline__ void nv_group_bf16(const unsigned c[4], const float sbv[2], float g, unsigned o[8]) {
+  const float kf[2] = {sbv[0] / g, sbv[1] / g};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    unsigned e[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) e[k] = bf16_rne(decode_code<0>((c[q] >> (4 * k)) & 0xFu, 0) * kf[q >> 1]);
+    o[2 * q] = e[0] | (e[1] << 16);
+    o[2 * q + 1] = e[2] | (e[3] << 16);
+  }
+  swap_halves(o[0], o[2]);
+  swap_halves(o[1], o[3]);
+  swap_halves(o[4], o[6]);
+  swap_halves(o[5], o[7]);
+}
+
 // E2M1 codes of one group: on return the lower lane holds bytes 0-7 of the
 // group's 16 code bytes (w[0], w[1]), the upper lane bytes 8-15.
 __device__ __forceinline__ void group_fp4_bytes(const unsigned c[4], unsigned sb, unsigned w[2]) {
@@ -148,14 +189,17 @@ __device__ __forceinline__ void group_fp8_bytes(const unsigned c[4], unsigned sb
 }
 
 // bf16 source, OP_QDQ (bf16 out) or OP_QUANT, staged through LDS.
+// FMT: 0 = MXFP4, 1 = MXFP8, 2 = NVFP4 (16-groups, E4M3 scales and the
+// per-tensor multiplier *gp).
 // SL (OP_QUANT only): 0 = row-major scales, 1 = the blocked layout `bl`.
 template <int FMT, int OP, int RB, int THREADS, int SL>
 __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict__ src,
                                                       const uint16_t *__restrict__ rot, int r,
                                                       void *__restrict__ dst, uint8_t *__restrict__ codes,
                                                       uint8_t *__restrict__ scales, int64_t n_blk,
-                                                      BlockedScales bl) {
+                                                      BlockedScales bl, const float *__restrict__ gp) {
   constexpr int NJT = RB / 32, NKB = RB / 16;
+  constexpr bool FP4 = FMT != 1;      // E2M1 codes (MXFP4 and NVFP4)
   constexpr int C = RB / 8;           // 16-byte input pieces per block
   constexpr int TP = 32 * C;          // input pieces per tile (= 64 * NKB)
   constexpr int WAVES = THREADS / 64;
@@ -202,6 +246,11 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
 
   const int lane = threadIdx.x & 63, h = lane >> 5, n = lane & 31;
   u32x4 *T = sT[threadIdx.x >> 6];
+  float g = 0.0f, c6 = 0.0f;
+  if constexpr (FMT == 2) {
+    g = *gp;
+    c6 = g / 6.0f;
+  }
   const int64_t n_elem = n_blk * RB;
   const int64_t n_tiles = (n_blk + 31) / 32;
   const int64_t stride = (int64_t)gridDim.x * WAVES;
@@ -239,7 +288,7 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
     wave_lds_sync();
     // 3. rotate, quantize, and place the outputs in LDS
     const int64_t blk = tile * 32 + n;
-    unsigned sbw = 0;
+    uint64_t sbw = 0;  // the block's scale bytes, in order
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) {
       f32x16 acc = {};
@@ -250,14 +299,23 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
       {
         unsigned sb, c[4];
         float sc;
-        group_codes<FMT>(acc, sb, sc, c);
-        sbw |= sb << (8 * jt);
+        unsigned o[8];
+        if constexpr (FMT == 2) {
+          unsigned sb2[2];
+          float sbv[2];
+          nv_group_codes(acc, g, c6, sb2, sbv, c);
+          sb = 0u;  // never the NaN marker
+          sbw |= (uint64_t)(sb2[0] | (sb2[1] << 8)) << (16 * jt);
+          if (OP == OP_QDQ) nv_group_bf16(c, sbv, g, o);
+        } else {
+          group_codes<FMT>(acc, sb, sc, c);
+          sbw |= (uint64_t)sb << (8 * jt);
+          if (OP == OP_QDQ) group_bf16<FMT>(c, sb, sc, o);
+        }
         if (OP == OP_QDQ) {
-          unsigned o[8];
-          group_bf16<FMT>(c, sb, sc, o);
           T[swz<C>(n * C + 4 * jt + h)] = u32x4{o[0], o[1], o[2], o[3]};
           T[swz<C>(n * C + 4 * jt + 2 + h)] = u32x4{o[4], o[5], o[6], o[7]};
-        } else if (FMT == 0) {
+        } else if (FP4) {
           unsigned w[2];
           group_fp4_bytes(c, sb, w);
           ((u32x2 *)T)[2 * swz<C4>(n * C4 + jt) + h] = u32x2{w[0], w[1]};
@@ -273,8 +331,16 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
       const int64_t gf0 = blk * NJT, i = gf0 / bl.groups, g0 = gf0 - i * bl.groups;
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt) scales[blocked_offset(i, g0 + jt, bl.gblocks)] = (uint8_t)(sbw >> (8 * jt));
+    } else if (OP == OP_QUANT && FMT == 2 && h == 0 && blk < n_blk) {
+      // RB/16 bytes per block
+      if (NJT == 4) {
+        *(unsigned *)(scales + blk * 8) = (unsigned)sbw;  // scales are 4-byte aligned
+        *(unsigned *)(scales + blk * 8 + 4) = (unsigned)(sbw >> 32);
+      }
+      else if (NJT == 2) *(unsigned *)(scales + blk * 4) = (unsigned)sbw;
+      else *(uint16_t *)(scales + blk * 2) = (uint16_t)sbw;
     } else if (OP == OP_QUANT && h == 0 && blk < n_blk) {
-      if (NJT == 4) *(unsigned *)(scales + blk * 4) = sbw;
+      if (NJT == 4) *(unsigned *)(scales + blk * 4) = (unsigned)sbw;
       else if (NJT == 2) *(uint16_t *)(scales + blk * 2) = (uint16_t)sbw;
       else scales[blk] = (uint8_t)sbw;
     }
@@ -294,8 +360,8 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
           if (e_tile + (int64_t)(q * 64 + lane) * 8 < n_elem) __builtin_nontemporal_store(o[q], g + q * 64);
       }
     } else {
-      constexpr int CP = FMT == 0 ? C4 : C8;      // code pieces per block
-      constexpr int EPP = FMT == 0 ? 32 : 16;     // elements per code piece
+      constexpr int CP = FP4 ? C4 : C8;           // code pieces per block
+      constexpr int EPP = FP4 ? 32 : 16;          // elements per code piece
       constexpr int NQ = (32 * CP + 63) / 64;
       u32x4 *g = (u32x4 *)(codes + e_tile / EPP * 16) + lane;
       u32x4 o[NQ];
@@ -448,19 +514,19 @@ static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
 
 template <int FMT, int OP, int RB>
 static void run_staged(const void *src, const void *rot, int r, void *dst, uint8_t *codes, uint8_t *scales,
-                       int64_t n, hipStream_t st, const BlockedScales *bl) {
+                       int64_t n, hipStream_t st, const BlockedScales *bl, const float *gp = nullptr) {
   using Cfg = StagedCfg<RB>;
   const int64_t n_blk = n / RB;
   const unsigned g = persistent_grid((n_blk + 31) / 32, Cfg::threads / 64, Cfg::per_cu);
-  if constexpr (OP == OP_QUANT) {
+  if constexpr (OP == OP_QUANT && FMT != 2) {
     if (bl != nullptr) {
       k_rot_bf16<FMT, OP, RB, Cfg::threads, 1><<<g, Cfg::threads, 0, st>>>(
-          (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, *bl);
+          (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, *bl, nullptr);
       return;
     }
   }
   k_rot_bf16<FMT, OP, RB, Cfg::threads, 0><<<g, Cfg::threads, 0, st>>>(
-      (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, BlockedScales{0, 0, 0});
+      (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, BlockedScales{0, 0, 0}, gp);
 }
 
 template <int FMT, int OP, int RB>
@@ -486,6 +552,21 @@ static void dispatch_rb(int dtype, const void *src, const void *rot, int r, void
     else if (rb == 64) run_direct<FMT, OP, 64>(dtype, src, rot, r, dst, n, st);
     else run_direct<FMT, OP, 128>(dtype, src, rot, r, dst, n, st);
   }
+}
+
+hipError_t launch_nv_rot(int op, const void *src, const void *rot, int r, void *dst, uint8_t *codes,
+                         uint8_t *scales, const float *gp, int64_t n, hipStream_t st) {
+  const int rb = r < 32 ? 32 : r;
+  if (op == OP_QDQ) {
+    if (rb == 32) run_staged<2, OP_QDQ, 32>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
+    else if (rb == 64) run_staged<2, OP_QDQ, 64>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
+    else run_staged<2, OP_QDQ, 128>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
+  } else {
+    if (rb == 32) run_staged<2, OP_QUANT, 32>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
+    else if (rb == 64) run_staged<2, OP_QUANT, 64>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
+    else run_staged<2, OP_QUANT, 128>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_rot(int fmt, int op, int dtype, const void *src, const void *rot, int r, void *dst,

@@ -180,6 +180,66 @@ def rotate_within_beta(y_gpu: np.ndarray, y: np.ndarray, beta: np.ndarray) -> fl
     return worst
 
 
+# ---- the band of the rotated NVFP4 path ---------------------------------------
+
+def _f32_down(v):
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    return np.where(f.astype(np.float64) > v, np.nextafter(f, np.float32(-np.inf)), f).astype(np.float32)
+
+
+def _f32_up(v):
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    return np.where(f.astype(np.float64) < v, np.nextafter(f, np.float32(np.inf)), f).astype(np.float32)
+
+
+def nv_band_check(y: np.ndarray, beta: np.ndarray, g: float, *, deq_gpu=None, codes_gpu=None,
+                  scales_gpu=None) -> dict:
+    """The band of the rotated path for NVFP4: with |y_gpu - y| <= beta, a
+    16-group's E4M3 scale byte lies between those of its smallest and largest
+    possible abs-max (the scale is monotone in amax), and under the GPU's
+    scale each element lies between the values of y - beta and y + beta (the
+    code is monotone in x).  Pass deq_gpu (QDQ output values, bf16 as
+    float64) or codes_gpu (unpacked [M, K]) with scales_gpu ([M, K/16])."""
+    M, K = y.shape
+    G = M * K // 16
+    yg, bg = y.reshape(G, 16), beta.reshape(G, 16)
+    sb_lo = oracle.nv_scale_byte_n(g, _f32_down(np.max(np.maximum(np.abs(yg) - bg, 0.0), axis=1)))
+    sb_hi = oracle.nv_scale_byte_n(g, _f32_up(np.max(np.abs(yg) + bg, axis=1)))
+    y32 = yg.astype(np.float32)
+    sb_ex = oracle.nv_scale_byte_n(g, np.abs(y32).max(axis=1))
+    code_ex = oracle.nv_code_n(g, np.repeat(sb_ex, 16).reshape(G, 16), y32)
+    lo_x, hi_x = _f32_down(yg - bg), _f32_up(yg + bg)
+    if codes_gpu is not None:
+        sb = scales_gpu.reshape(G)
+        bad = (sb < sb_lo) | (sb > sb_hi)
+        assert not bad.any(), f"{bad.sum()} NVFP4 scales outside the band"
+        sbr = np.repeat(sb, 16).reshape(G, 16)
+        c = codes_gpu.reshape(G, 16)
+        v, vlo, vhi = (code_values(E2M1, cc) for cc in (c, oracle.nv_code_n(g, sbr, lo_x),
+                                                        oracle.nv_code_n(g, sbr, hi_x)))
+        ok = (v >= vlo) & (v <= vhi)
+        assert ok.all(), f"{(~ok).sum()} NVFP4 codes outside the band"
+        differ = (c != code_ex) | (sb != sb_ex)[:, None]
+    else:
+        d = deq_gpu.reshape(G, 16)
+        group_ok = np.zeros(G, dtype=bool)
+        for cand in range(int(sb_lo.min()), int(sb_hi.max()) + 1):
+            idx = np.flatnonzero((sb_lo <= cand) & (cand <= sb_hi))
+            if idx.size == 0:
+                continue
+            sbr = np.full((idx.size, 16), cand, dtype=np.uint8)
+            vlo = f64_to_bf16_values(oracle.nv_value_n(g, sbr, oracle.nv_code_n(g, sbr, lo_x[idx])).astype(np.float64))
+            vhi = f64_to_bf16_values(oracle.nv_value_n(g, sbr, oracle.nv_code_n(g, sbr, hi_x[idx])).astype(np.float64))
+            group_ok[idx] |= ((d[idx] >= vlo) & (d[idx] <= vhi)).all(axis=1)
+        assert group_ok.all(), f"{(~group_ok).sum()} NVFP4 groups outside the band"
+        ev = f64_to_bf16_values(oracle.nv_value_n(g, np.repeat(sb_ex, 16).reshape(G, 16), code_ex).astype(np.float64))
+        differ = d != ev
+    out = {"elements": M * K, "differ": int(differ.sum()), "ambiguous_scale_groups": int((sb_lo != sb_hi).sum())}
+    frac = out["differ"] / max(1, out["elements"])
+    assert frac <= 1e-4, f"{out['differ']} NVFP4 elements ({frac:.2e}) differ from the oracle (limit 1e-4)"
+    return out
+
+
 # ---- the scaled-MFMA GEMM error bound ----------------------------------------
 
 def gemm_error_bound(fmt: int, a_dq: np.ndarray, b_dq: np.ndarray) -> np.ndarray:

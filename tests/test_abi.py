@@ -29,6 +29,9 @@ def lib():
     L.mx_blocked_scales_bytes.restype = i64
     L.mx_scales_to_blocked.argtypes = [vp, i64, i64, vp]
     L.mx_quantize_blocked.argtypes = [i, vp, i64, i64, vp, i, vp, vp]
+    L.mx_nvfp4_quantize.argtypes = [vp, i64, i64, vp, i, vp, vp, vp]
+    L.mx_nvfp4_qdq.argtypes = [vp, i64, i64, vp, i, vp, vp]
+    L.mx_nvfp4_dequantize.argtypes = [vp, vp, i64, i64, vp, i, vp]
     L.mx_set_stream.argtypes = [vp]
     L.mx_get_stream.restype = vp
     L.mx_status_string.argtypes = [i]
@@ -44,7 +47,8 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     names = set(declared_symbols())
     assert {"mx_qdq", "mx_quantize", "mx_dequantize", "mx_rotate", "mx_matmul", "mx_blocked_scales_bytes",
-            "mx_scales_to_blocked", "mx_quantize_blocked", "mx_set_stream",
+            "mx_scales_to_blocked", "mx_quantize_blocked", "mx_nvfp4_quantize", "mx_nvfp4_qdq",
+            "mx_nvfp4_dequantize", "mx_set_stream",
             "mx_get_stream", "mx_status_string"} <= names
 
 
@@ -142,6 +146,24 @@ def test_blocked_scales_size_and_errors(lib):
     assert lib.mx_quantize_blocked(1, A + 8, 4, 64, None, 0, A, A) == MX_EALIGN
 
 
+def test_nvfp4_argument_errors(lib):
+    assert lib.mx_nvfp4_quantize(A, 4, 40, None, 0, A, A, A) == MX_ESHAPE
+    assert lib.mx_nvfp4_quantize(A, -1, 32, None, 0, A, A, A) == MX_ESHAPE
+    assert lib.mx_nvfp4_quantize(A, 4, 48, A, 16, A, A, A) == MX_EROT  # a rotation needs K % 32 == 0
+    assert lib.mx_nvfp4_quantize(A, 4, 64, A, 48, A, A, A) == MX_EROT
+    assert lib.mx_nvfp4_quantize(A, 4, 64, None, 16, A, A, A) == MX_EROT
+    assert lib.mx_nvfp4_quantize(A, 4, 48, None, 0, None, A, A) == MX_ENULL
+    assert lib.mx_nvfp4_quantize(A, 4, 48, None, 0, A, A, None) == MX_ENULL
+    assert lib.mx_nvfp4_quantize(A + 8, 4, 48, None, 0, A, A, A) == MX_EALIGN
+    assert lib.mx_nvfp4_quantize(A, 4, 48, None, 0, A + 2, A, A) == MX_EALIGN
+    assert lib.mx_nvfp4_quantize(A, 4, 48, None, 0, A, A, A + 2) == MX_EALIGN
+    assert lib.mx_nvfp4_qdq(A, 4, 24, None, 0, A, A) == MX_ESHAPE
+    assert lib.mx_nvfp4_qdq(A, 4, 48, None, 0, A, A + 4) == MX_EALIGN
+    assert lib.mx_nvfp4_dequantize(A, A, 4, 48, A, 3, A) == MX_EDTYPE
+    assert lib.mx_nvfp4_dequantize(A, A, 4, 40, A, 0, A) == MX_ESHAPE
+    assert lib.mx_nvfp4_dequantize(A, None, 4, 48, A, 0, A) == MX_ENULL
+
+
 def test_empty_is_a_noop(lib):
     # no pointer is touched and no kernel is launched for M == 0 or K == 0
     assert lib.mx_qdq(0, None, 0, 0, 64, None, 0, None) == MX_OK
@@ -153,6 +175,9 @@ def test_empty_is_a_noop(lib):
     assert lib.mx_matmul(1, None, None, None, None, 1, 8, 0, 64, 1.0, 1, None) == MX_OK
     assert lib.mx_scales_to_blocked(None, 0, 64, None) == MX_OK
     assert lib.mx_quantize_blocked(0, None, 5, 0, None, 0, None, None) == MX_OK
+    assert lib.mx_nvfp4_quantize(None, 0, 48, None, 0, None, None, None) == MX_OK
+    assert lib.mx_nvfp4_qdq(None, 7, 0, None, 0, None, None) == MX_OK
+    assert lib.mx_nvfp4_dequantize(None, None, 0, 16, None, 1, None) == MX_OK
 
 
 def test_status_strings_and_stream(lib):

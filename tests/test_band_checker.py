@@ -67,3 +67,42 @@ def test_rotate_tolerance_check(case):
     bad.ravel()[i] += np.float32(3 * beta.ravel()[i])
     with pytest.raises(AssertionError):
         rotate_within_beta(bad, y, beta)
+
+
+# ---- the NVFP4 band ------------------------------------------------------------
+
+from _parity import nv_band_check  # noqa: E402
+
+G_NV = 37.5
+
+
+def test_nvfp4_accepts_oracle_output(case):
+    x, R, y, beta = case
+    d = bf16_values(oracle.nv_qdq(x, G_NV, R, 64))
+    assert nv_band_check(y, beta, G_NV, deq_gpu=d)["differ"] == 0
+    codes, scales = oracle.nv_quantize(x, G_NV, R, 64)
+    st = nv_band_check(y, beta, G_NV, codes_gpu=unpack_codes(E2M1, codes, x.shape[1]), scales_gpu=scales)
+    assert st["differ"] == 0
+
+
+def test_nvfp4_rejects_planted_value(case):
+    x, R, y, beta = case
+    d = bf16_values(oracle.nv_qdq(x, G_NV, R, 64))
+    big = np.argmax(np.abs(d))
+    d.ravel()[big] *= 0.5
+    with pytest.raises(AssertionError):
+        nv_band_check(y, beta, G_NV, deq_gpu=d)
+
+
+def test_nvfp4_rejects_planted_scale_and_code(case):
+    x, R, y, beta = case
+    codes, scales = oracle.nv_quantize(x, G_NV, R, 64)
+    bad = scales.copy()
+    bad[2, 7] += 1
+    with pytest.raises(AssertionError):
+        nv_band_check(y, beta, G_NV, codes_gpu=unpack_codes(E2M1, codes, x.shape[1]), scales_gpu=bad)
+    u = unpack_codes(E2M1, codes, x.shape[1]).copy()
+    k = int(np.argmax(np.abs(y)))
+    u.ravel()[k] = (u.ravel()[k] & 8) | max(0, (u.ravel()[k] & 7) - 2)  # two grid steps smaller
+    with pytest.raises(AssertionError):
+        nv_band_check(y, beta, G_NV, codes_gpu=u, scales_gpu=scales)
