@@ -186,6 +186,11 @@ __device__ __forceinline__ unsigned bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two fp32 -> a packed bf16 pair, nearest-even (the hardware conversion).
+__device__ __forceinline__ unsigned bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 // ---- NVFP4 scale steps --------------------------------------------------------
 
 // E4M3 scale byte of q >= 0, nearest-even and saturating (the hardware
@@ -197,6 +202,15 @@ __device__ __forceinline__ unsigned nv_scale_byte(float q) {
 
 // fp32 value of a (non-negative) E4M3 scale byte.
 __device__ __forceinline__ float nv_scale_value(unsigned sb) { return decode_mag<1>(sb, 0); }
+
+// Dequantized NVFP4 pair as packed bf16: E2M1 nibbles 2*BYTE and 2*BYTE+1
+// of the code word c (exact values from the hardware conversion with scale
+// 1), each times kf (fp32, nearest-even), then nearest-even to bf16.
+template <int BYTE>
+__device__ __forceinline__ unsigned nv_bf16_pair(unsigned c, float kf) {
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, BYTE);
+  return bf16x2_rne(v.x * kf, v.y * kf);
+}
 
 // ---- blocked scale layout ---------------------------------------------------
 // The operand order of the 32x32x64 scaled MFMA: rows padded to 32, groups

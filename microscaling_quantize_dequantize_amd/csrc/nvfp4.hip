@@ -17,14 +17,12 @@
 
 namespace mx {
 
-namespace {
-
 constexpr int64_t NV_MAX_BLOCKS = (int64_t)1 << 22;
 constexpr int NV_T = 128;
 
 // E2M1 codes of the 8 bf16 values of a piece times m (8 nibbles, element 0
 // in bits 3:0).
-__device__ __forceinline__ unsigned nv_codes(u32x4 w, float m) {
+static __device__ __forceinline__ unsigned nv_codes(u32x4 w, float m) {
   const unsigned u[4] = {w.x, w.y, w.z, w.w};
   float v[8];
 #pragma unroll
@@ -39,8 +37,13 @@ __device__ __forceinline__ unsigned nv_codes(u32x4 w, float m) {
 }
 
 // Dequantized fp32 value of nibble k of c.
-__device__ __forceinline__ float nv_value(unsigned c, int k, float kf) {
+static __device__ __forceinline__ float nv_value(unsigned c, int k, float kf) {
   return decode_code<0>((c >> (4 * k)) & 0xFu, 0) * kf;
+}
+
+// The 8 dequantized values of a code word as bf16.
+static __device__ __forceinline__ u32x4 nv_bf16x8(unsigned c, float kf) {
+  return u32x4{nv_bf16_pair<0>(c, kf), nv_bf16_pair<1>(c, kf), nv_bf16_pair<2>(c, kf), nv_bf16_pair<3>(c, kf)};
 }
 
 template <int OP>
@@ -68,11 +71,8 @@ __global__ __launch_bounds__(NV_T) void k_nv_unrot(const u32x4 *__restrict__ src
     const float m = sbv == 0.0f ? 0.0f : g / sbv;
     const unsigned c = nv_codes(w, m);
     if (OP == OP_QDQ) {
-      const float kf = sbv / g;
-      unsigned o[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] = bf16_rne(nv_value(c, 2 * k, kf)) | (bf16_rne(nv_value(c, 2 * k + 1, kf)) << 16);
-      if (p < n_pieces) __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, dst + p);
+      const u32x4 o = nv_bf16x8(c, sbv / g);
+      if (p < n_pieces) __builtin_nontemporal_store(o, dst + p);
     } else {
       if (p < n_pieces) __builtin_nontemporal_store(c, (unsigned *)codes + p);
       // scale bytes: lanes 8k..8k+7 hold 4 consecutive groups; gather the 4
@@ -105,10 +105,7 @@ __global__ __launch_bounds__(NV_T) void k_nv_dequant(const uint8_t *__restrict__
     const float kf = nv_scale_value(scales[p >> 1]) / g;
     const unsigned c = __builtin_nontemporal_load((const unsigned *)codes + p);
     if (DT == 0) {
-      unsigned o[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] = bf16_rne(nv_value(c, 2 * k, kf)) | (bf16_rne(nv_value(c, 2 * k + 1, kf)) << 16);
-      __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, (u32x4 *)dst + p);
+      __builtin_nontemporal_store(nv_bf16x8(c, kf), (u32x4 *)dst + p);
     } else {
       unsigned v[8];
 #pragma unroll
@@ -120,12 +117,10 @@ __global__ __launch_bounds__(NV_T) void k_nv_dequant(const uint8_t *__restrict__
   }
 }
 
-unsigned nv_grid(int64_t n_pieces) {
+static unsigned nv_grid(int64_t n_pieces) {
   const int64_t want = (n_pieces + NV_T - 1) / NV_T;
   return (unsigned)(want < NV_MAX_BLOCKS ? want : NV_MAX_BLOCKS);
 }
-
-}  // namespace
 
 hipError_t launch_nv_unrot(int op, const void *src, void *dst, uint8_t *codes, uint8_t *scales, const float *g,
                            int64_t n, hipStream_t stream) {

@@ -149,11 +149,8 @@ __device__ __forceinline__ void nv_group_bf16(const unsigned c[4], const float s
   const float kf[2] = {sbv[0] / g, sbv[1] / g};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    unsigned e[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) e[k] = bf16_rne(decode_code<0>((c[q] >> (4 * k)) & 0xFu, 0) * kf[q >> 1]);
-    o[2 * q] = e[0] | (e[1] << 16);
-    o[2 * q + 1] = e[2] | (e[3] << 16);
+    o[2 * q] = nv_bf16_pair<0>(c[q], kf[q >> 1]);
+    o[2 * q + 1] = nv_bf16_pair<1>(c[q], kf[q >> 1]);
   }
   swap_halves(o[0], o[2]);
   swap_halves(o[1], o[3]);
