@@ -6,7 +6,8 @@
 // the dequantized operands multiplied in high precision ("[Transform]
 // [Quantization] Add QuTLASS support to vLLM", Purpose: MXFP4 matmul kernel;
 // review of the MXFP4 test).  A is [M x K] and B is [N x K], both in the
-// layout mx_quantize writes (row-major codes, unpadded [rows x K/32] scales).
+// layout mx_quantize writes (row-major codes; scales row-major [rows x K/32]
+// or in the blocked layout).
 //
 // Operand layout of the scaled MFMA (characterised on gfx950): in a 64-deep
 // k-step, lane l supplies row (or column) l%32 and
@@ -17,9 +18,16 @@
 // So the row-major code layout feeds the matrix cores directly: no
 // reordering of codes or scales is needed.
 //
-// Tiling: a 256-thread workgroup owns a 128 x 128 tile of C; each wave a
-// 64 x 64 quarter (2 x 2 MFMA tiles).  128-deep k-slices of A and B are
-// staged in LDS (rows padded by 16 bytes, conflict-free 16-byte reads).
+// Tiling: a 256-thread workgroup (one wave per SIMD) owns a 256 x 256 tile
+// of C; each wave a 128 x 128 quarter as 4 x 4 MFMA tiles, so that a k-step
+// reads 8 fragments from LDS for 16 MFMAs.  K-slices of 64 code bytes per row
+// are double-buffered in LDS (rows padded by 16 bytes): while the matrix
+// cores work on slice k, slice k+1 is written to the other buffer from
+// registers and slice k+2 is loaded from memory into those registers; the
+// fragments of each k-step are read from LDS while the MFMAs of the previous
+// step run (two register sets, one barrier per slice).
+#include <type_traits>
+
 #include "launch.h"
 #include "mx_device.h"
 
@@ -27,9 +35,23 @@ namespace mx {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int GT = 256, BM = 128, BN = 128, BK = 128;
+constexpr int GT = 256, TI = 4, TJ = 4;               // threads; MFMA tiles per wave (rows, columns)
+constexpr int BM = 64 * TI, BN = 64 * TJ;             // workgroup tile
 
-// SL 0: row-major [rows x K/32] scales, staged through LDS per k-slice;
+// A k-slice is 64 code bytes of every row: 128 k of E2M1 (two MFMA k-steps)
+// or 64 k of E4M3 (one k-step, twice as long on the matrix cores).
+template <int FMT>
+struct GemmShape {
+  static constexpr int BK = FMT == 0 ? 128 : 64;      // k per slice
+  static constexpr int RB = 64;                       // code bytes per row per k-slice
+  static constexpr int LDR = RB + 16;                 // padded LDS row stride
+  static constexpr int CH = RB / 16;                  // 16-byte chunks per row
+  static constexpr int NCA = BM * CH / GT;            // chunks per thread, A
+  static constexpr int NCB = BN * CH / GT;            // chunks per thread, B
+  static constexpr int BUF = (BM + BN) * LDR;         // bytes per LDS buffer
+};
+
+// SL 0: row-major [rows x K/32] scales, staged through LDS with the codes;
 // SL 1: the blocked layout, where a lane's word for its row block and
 // 256-deep k-span is one coalesced 32-bit load.
 template <int FMT, int OUT, int SL>
@@ -37,103 +59,215 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
                                                  const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
                                                  int64_t M, int64_t N, int64_t K, float alpha,
                                                  void *__restrict__ C) {
-  constexpr int RB = FMT == 0 ? BK / 2 : BK;  // code bytes per row per k-slice
-  constexpr int LDR = RB + 16;                // padded LDS row stride
-  constexpr int CH = RB / 16;                 // 16-byte chunks per row
-  constexpr int GS = BK / 32;                 // scale groups per row per k-slice
-  constexpr int CBSZ = FMT == 0 ? 4 : 0;      // FP4 E2M1 : FP8 E4M3
-  __shared__ __attribute__((aligned(16))) uint8_t sA[BM * LDR];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[BN * LDR];
-  __shared__ uint8_t sSA[BM * GS], sSB[BN * GS];
+  using S = GemmShape<FMT>;
+  constexpr int BK = S::BK;
+  constexpr int CBSZ = FMT == 0 ? 4 : 0;  // FP4 E2M1 : FP8 E4M3
+  __shared__ __attribute__((aligned(16))) uint8_t sm[2 * S::BUF];
+  __shared__ __attribute__((aligned(4))) uint8_t ss[2][BM + BN][4];  // row-major scales of a slice (SL 0)
+  __shared__ unsigned sw[2][4][TI + TJ][64];                         // each wave's blocked words (SL 1)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, h = lane >> 5;
   const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave >> 1) * (32 * TI), wn = (wave & 1) * (32 * TJ);
   const int64_t rowbytes = FMT == 0 ? K / 2 : K;
   const int64_t groups = K / 32;
   const int64_t gblocks = (groups + 7) / 8;
+  const int nslices = (int)((K + BK - 1) / BK);
 
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  // ---- registers in flight: the codes (and scales) of one k-slice --------
+  u32x4 pa[S::NCA], pb[S::NCB];
+  unsigned psa = 0x7F7F7F7Fu, psb = 0x7F7F7F7Fu;  // SL 0: this thread's row's 4 scale bytes
+  unsigned pwa[TI], pwb[TJ];                      // SL 1: this lane's blocked words
 
-  for (int64_t k0 = 0; k0 < K; k0 += BK) {
-    const int64_t kb0 = FMT == 0 ? k0 / 2 : k0;  // byte offset of the slice in a row
+  const bool interior = m0 + BM <= M && n0 + BN <= N;  // wave-uniform
+  auto load_slice = [&](int ks) {
+    const int64_t k0 = (int64_t)ks * BK, kb0 = FMT == 0 ? k0 / 2 : k0;
+    if (kb0 >= rowbytes) return;  // past the end: nothing to load
+    if (interior && kb0 + S::RB <= rowbytes) {
+      // a whole slice inside the operands: no per-chunk bounds
 #pragma unroll
-    for (int it = 0; it < BM * CH / GT; ++it) {
-      const int idx = tid + it * GT, row = idx / CH, c = idx % CH;
-      const int64_t kb = kb0 + 16 * c;
-      u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
-      if (m0 + row < M && kb < rowbytes) va = *(const u32x4 *)(A + (m0 + row) * rowbytes + kb);
-      if (n0 + row < N && kb < rowbytes) vb = *(const u32x4 *)(B + (n0 + row) * rowbytes + kb);
-      *(u32x4 *)(sA + row * LDR + 16 * c) = va;
-      *(u32x4 *)(sB + row * LDR + 16 * c) = vb;
-    }
-    // rows past the end and groups past K hold zero codes; any finite scale will do
-    unsigned wa[2] = {0x7F7F7F7Fu, 0x7F7F7F7Fu}, wb[2] = {0x7F7F7F7Fu, 0x7F7F7F7Fu};
-    if (SL == 0) {
+      for (int it = 0; it < S::NCA; ++it) {
+        const int idx = tid + it * GT, row = idx / S::CH, c = idx % S::CH;
+        pa[it] = *(const u32x4 *)(A + (m0 + row) * rowbytes + kb0 + 16 * c);
+      }
 #pragma unroll
-      for (int it = 0; it < BM * GS / GT; ++it) {
-        const int idx = tid + it * GT, row = idx / GS, gg = idx % GS;
-        const int64_t g = k0 / 32 + gg;
-        sSA[idx] = (m0 + row < M && g < groups) ? As[(m0 + row) * groups + g] : (uint8_t)127;
-        sSB[idx] = (n0 + row < N && g < groups) ? Bs[(n0 + row) * groups + g] : (uint8_t)127;
+      for (int it = 0; it < S::NCB; ++it) {
+        const int idx = tid + it * GT, row = idx / S::CH, c = idx % S::CH;
+        pb[it] = *(const u32x4 *)(B + (n0 + row) * rowbytes + kb0 + 16 * c);
       }
     } else {
-      // row blocks exist up to the one holding the last row; padding groups hold 127
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int64_t ra = m0 + wm + 32 * i, rb = n0 + wn + 32 * i;
-        if (ra < M) wa[i] = ((const unsigned *)As)[((ra >> 5) * gblocks + (k0 >> 8)) * 64 + lane];
-        if (rb < N) wb[i] = ((const unsigned *)Bs)[((rb >> 5) * gblocks + (k0 >> 8)) * 64 + lane];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < BK / 64; ++s) {
-      i32x8 fa[2], fb[2];
-      int sa[2], sb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ra = wm + 32 * i + r, rb = wn + 32 * i + r;
-        u32x4 a0, a1 = {0u, 0u, 0u, 0u}, b0, b1 = {0u, 0u, 0u, 0u};
-        if (FMT == 0) {
-          a0 = *(const u32x4 *)(sA + ra * LDR + 32 * s + 16 * h);
-          b0 = *(const u32x4 *)(sB + rb * LDR + 32 * s + 16 * h);
-        } else {
-          a0 = *(const u32x4 *)(sA + ra * LDR + 64 * s + 16 * h);
-          a1 = *(const u32x4 *)(sA + ra * LDR + 64 * s + 32 + 16 * h);
-          b0 = *(const u32x4 *)(sB + rb * LDR + 64 * s + 16 * h);
-          b1 = *(const u32x4 *)(sB + rb * LDR + 64 * s + 32 + 16 * h);
-        }
-        fa[i] = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        fb[i] = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-        if (SL == 0) {
-          sa[i] = sSA[ra * GS + 2 * s + h];  // this lane's group of the 64-deep step
-          sb[i] = sSB[rb * GS + 2 * s + h];
-        } else {
-          const int sh = 8 * ((int)((k0 >> 6) & 3) + s);  // k-step within the 256-deep span
-          sa[i] = (int)((wa[i] >> sh) & 0xFFu);
-          sb[i] = (int)((wb[i] >> sh) & 0xFFu);
-        }
+      for (int it = 0; it < S::NCA; ++it) {
+        const int idx = tid + it * GT, row = idx / S::CH, c = idx % S::CH;
+        const int64_t kb = kb0 + 16 * c;
+        pa[it] = (m0 + row < M && kb < rowbytes) ? *(const u32x4 *)(A + (m0 + row) * rowbytes + kb)
+                                                 : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], CBSZ, CBSZ, 0,
-                                                                      sa[i], 0, sb[j]);
+      for (int it = 0; it < S::NCB; ++it) {
+        const int idx = tid + it * GT, row = idx / S::CH, c = idx % S::CH;
+        const int64_t kb = kb0 + 16 * c;
+        pb[it] = (n0 + row < N && kb < rowbytes) ? *(const u32x4 *)(B + (n0 + row) * rowbytes + kb)
+                                                 : u32x4{0u, 0u, 0u, 0u};
+      }
     }
+    // rows past the end and groups past K hold zero codes; any finite scale will do
+    if (SL == 0) {
+      unsigned wa = 0x7F7F7F7Fu, wb = 0x7F7F7F7Fu;
+#pragma unroll
+      for (int j = 0; j < BK / 32; ++j) {
+        const int64_t g = k0 / 32 + j;
+        const unsigned va = (m0 + tid < M && g < groups) ? As[(m0 + tid) * groups + g] : 127u;
+        const unsigned vb = (n0 + tid < N && g < groups) ? Bs[(n0 + tid) * groups + g] : 127u;
+        wa = (wa & ~(0xFFu << (8 * j))) | (va << (8 * j));
+        wb = (wb & ~(0xFFu << (8 * j))) | (vb << (8 * j));
+      }
+      psa = wa;
+      psb = wb;
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int64_t ra = m0 + wm + 32 * i;
+        pwa[i] = ra < M ? ((const unsigned *)As)[((ra >> 5) * gblocks + (k0 >> 8)) * 64 + lane] : 0x7F7F7F7Fu;
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int64_t rb = n0 + wn + 32 * j;
+        pwb[j] = rb < N ? ((const unsigned *)Bs)[((rb >> 5) * gblocks + (k0 >> 8)) * 64 + lane] : 0x7F7F7F7Fu;
+      }
+    }
+  };
+  auto store_slice = [&](int buf) {
+    uint8_t *sA = sm + buf * S::BUF, *sB = sA + BM * S::LDR;
+#pragma unroll
+    for (int it = 0; it < S::NCA; ++it) {
+      const int idx = tid + it * GT, row = idx / S::CH, c = idx % S::CH;
+      *(u32x4 *)(sA + row * S::LDR + 16 * c) = pa[it];
+    }
+#pragma unroll
+    for (int it = 0; it < S::NCB; ++it) {
+      const int idx = tid + it * GT, row = idx / S::CH, c = idx % S::CH;
+      *(u32x4 *)(sB + row * S::LDR + 16 * c) = pb[it];
+    }
+    if (SL == 0) {
+      *(unsigned *)ss[buf][tid] = psa;  // one thread per row (GT == BM == BN)
+      *(unsigned *)ss[buf][BM + tid] = psb;
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) sw[buf][wave][i][lane] = pwa[i];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) sw[buf][wave][TI + j][lane] = pwb[j];
+    }
+  };
+  static_assert(GT == BM && GT == BN, "one thread per row stages the row-major scales");
+
+  f32x16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+
+  // ---- fragments of one 64-deep k-step, two sets (steps alternate) -------
+  constexpr int NS = BK / 64;           // k-steps per slice
+  // E2M1 fragments are 16 bytes (the MFMA reads 4 registers); E4M3
+  // fragments 32 bytes, kept as one 8-register tuple
+  using Frag = typename std::conditional<FMT == 0, u32x4, i32x8>::type;
+  Frag fr[NS][TI + TJ];
+  int sc[NS][TI + TJ];
+  // fragments and scale bytes of k-step s of slice ks (LDS buffer buf)
+  auto read_frags = [&](auto P, int buf, int ks, int s) {
+    constexpr int p = decltype(P)::value;
+    const uint8_t *sA = sm + buf * S::BUF, *sB = sA + BM * S::LDR;
+    const int sh = 8 * ((int)(((int64_t)ks * BK >> 6) & 3) + s);  // k-step within the 256-deep span
+#pragma unroll
+    for (int f = 0; f < TI + TJ; ++f) {
+      const int row = (f < TI ? wm + 32 * f : wn + 32 * (f - TI)) + r;
+      const uint8_t *base = (f < TI ? sA : sB) + row * S::LDR + (FMT == 0 ? 32 : 64) * s + 16 * h;
+      if constexpr (FMT == 0) {
+        fr[p][f] = *(const u32x4 *)base;
+      } else {
+        const u32x4 lo = *(const u32x4 *)base, hi = *(const u32x4 *)(base + 32);
+        fr[p][f] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      if (SL == 0) sc[p][f] = (int)ss[buf][(f < TI ? 0 : BM) + row][2 * s + h];
+      else sc[p][f] = (int)((sw[buf][wave][f][lane] >> sh) & 0xFFu);
+    }
+  };
+  auto mfma_step = [&](auto P) {
+    constexpr int p = decltype(P)::value;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        i32x8 fa, fb;
+        if constexpr (FMT == 0) {
+          const u32x4 a = fr[p][i], b = fr[p][TI + j];  // upper halves unused for E2M1
+          fa = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+          fb = i32x8{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+        } else {
+          fa = fr[p][i];
+          fb = fr[p][TI + j];
+        }
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[i][j], CBSZ, CBSZ, 0, sc[p][i], 0,
+                                                                    sc[p][TI + j]);
+      }
+  };
+  // interleave the 16 MFMAs of a step with the LDS reads of the next one
+  auto interleave = [&]() {
+#pragma unroll
+    for (int k = 0; k < TI * TJ; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+    }
+  };
+  // the last k-step of slice ks: stage slice ks+1 into the other buffer and
+  // slice ks+2 into registers, synchronise, then read step 0 of slice ks+1
+  // while the matrix cores run step P.  Past the end the stores and reads
+  // touch only unused LDS and the loads are bounds-checked away.
+  auto last_step = [&](auto P, auto Q, int ks) {
+    const int buf = ks & 1;
+    store_slice(buf ^ 1);
+    load_slice(ks + 2);
     __syncthreads();
+    read_frags(Q, buf ^ 1, ks + 1, 0);
+    mfma_step(P);
+    interleave();
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+
+  load_slice(0);
+  store_slice(0);
+  load_slice(1);
+  __syncthreads();
+
+  if constexpr (NS == 2) {
+    // E2M1: two k-steps per slice, fragment sets 0 and 1 within each slice
+    read_frags(P0{}, 0, 0, 0);
+    for (int ks = 0; ks < nslices; ++ks) {
+      read_frags(P1{}, ks & 1, ks, 1);
+      mfma_step(P0{});
+      interleave();
+      last_step(P1{}, P0{}, ks);
+    }
+  } else {
+    // E4M3: one k-step per slice and one fragment set (two sets of 32-byte
+    // fragments do not fit beside the accumulators)
+    for (int ks = 0; ks < nslices; ++ks) {
+      read_frags(P0{}, ks & 1, ks, 0);
+      mfma_step(P0{});
+      store_slice((ks & 1) ^ 1);
+      load_slice(ks + 2);
+      __syncthreads();
+    }
   }
+
   // accumulator: lane l, register a holds C[8(a/4) + 4(l/32) + a%4][l%32]
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TJ; ++j) {
       const int64_t col = n0 + wn + 32 * j + r;
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
