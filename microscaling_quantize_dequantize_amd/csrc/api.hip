@@ -154,6 +154,7 @@ MX_API int mx_matmul(int fmt, const uint8_t *a_codes, const uint8_t *a_scales, c
     return st;
   if (scale_layout != MX_SCALES_ROWMAJOR && scale_layout != MX_SCALES_BLOCKED) return MX_ELAYOUT;
   if (M > ((int64_t)65535 << 7) || (N + 127) / 128 > (int64_t)INT32_MAX) return MX_ESHAPE;  // grid limits
+  if ((fmt == MX_FMT_E2M1 ? K / 2 : K) > ((int64_t)1 << 23)) return MX_ESHAPE;  // 32-bit buffer offsets
   if (M == 0 || N == 0) return MX_OK;
   if (!c) return MX_ENULL;
   if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return MX_ENULL;

@@ -120,6 +120,8 @@ def test_matmul_argument_errors(lib):
     assert lib.mx_matmul(0, A, A, A, A, 0, -1, 4, 64, F, 0, A) == MX_ESHAPE
     assert lib.mx_matmul(0, A, A, A, A, 0, 4, -4, 64, F, 0, A) == MX_ESHAPE
     assert lib.mx_matmul(1, A, A, A, A, 0, 65535 * 128 + 1, 4, 64, F, 1, A) == MX_ESHAPE
+    assert lib.mx_matmul(1, A, A, A, A, 0, 4, 4, (1 << 23) + 32, F, 0, A) == MX_ESHAPE  # 32-bit offsets
+    assert lib.mx_matmul(0, A, A, A, A, 0, 4, 4, (1 << 24) + 32, F, 0, A) == MX_ESHAPE
     assert lib.mx_matmul(0, A, A, A, A, 2, 4, 4, 64, F, 0, A) == MX_ELAYOUT
     assert lib.mx_matmul(0, A, A, A, A, 0, 4, 4, 64, F, 0, None) == MX_ENULL
     assert lib.mx_matmul(0, A, None, A, A, 0, 4, 4, 64, F, 0, A) == MX_ENULL
