@@ -20,25 +20,24 @@
 //
 // Tiling: a 256-thread workgroup (one wave per SIMD) owns a 256 x 256 tile
 // of C; each wave a 128 x 128 quarter as 4 x 4 MFMA tiles, so that a k-step
-// reads 8 fragments from LDS for 16 MFMAs.  A k-slice is 64 code bytes of
-// every row (two E2M1 k-steps or one E4M3 k-step: 1024 matrix-core cycles
-// per wave either way).
+// reads 8 fragments from LDS for 16 MFMAs.  A k-slice is 128 code bytes of
+// every row (four E2M1 or two E4M3 k-steps: 2048 matrix-core cycles per wave
+// either way).
 //
-// Pipeline, per k-slice j:
-//   global -> registers   buffer loads issued two slices ahead (two register
-//                         sets), out-of-range rows and the K tail read as
-//                         zero by the buffer unit, so the loop has no
-//                         branches;
-//   registers -> LDS      written into a ring of three buffers two slices
-//                         ahead of use;
-//   LDS -> registers      each k-step's fragments read while the matrix
-//                         cores run the previous k-step, including the first
-//                         k-step of slice j+1 during the last of slice j.
-// With three buffers one barrier per slice suffices, and it comes after the
-// slice's last MFMA: no matrix-core idle time waits on LDS reads.
-// LDS rows are 64 bytes with the 16-byte chunks XOR-swizzled by row
-// ((row/4)%4), which keeps both the chunk writes and the fragment reads free
-// of bank conflicts without padding.
+// Data path (measured on gfx950: with one workgroup per CU, loads of whole
+// 128-byte row segments stream about twice as fast as 64-byte ones, and LDS
+// writes from registers run at a third of the LDS read rate):
+//   codes go from global memory straight into LDS (buffer loads with an LDS
+//   destination), one wave instruction per 8 rows x 128 bytes, into one of
+//   two static LDS slots; rows past the operands and the K tail read as zero
+//   through the buffer resource;
+//   the fragments of each k-step are read from LDS while the matrix cores run
+//   the previous k-step;
+//   one barrier per slice, placed before its last k-step, publishes the next
+//   slice (loaded during this one), so that the last k-step's MFMAs overlap
+//   the reads of the next slice's first fragments.
+// LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by (row/2)%8,
+// which keeps the 16-lane fragment reads free of bank conflicts.
 #include <type_traits>
 
 #include "launch.h"
@@ -47,21 +46,22 @@
 namespace mx {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+#define MX_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int GT = 256, TI = 4, TJ = 4;               // threads; MFMA tiles per wave (rows, columns)
 constexpr int BM = 64 * TI, BN = 64 * TJ;             // workgroup tile
-constexpr int RB = 64;                                // code bytes per row per k-slice
-constexpr int TILE = BM * RB;                         // one operand's slice in LDS
-constexpr int BUF = 2 * TILE;                         // one ring slot (A then B)
-constexpr int NBUF = 3;                               // ring depth
-constexpr int CPT = BM * (RB / 16) / GT;              // 16-byte chunks per thread per operand
+constexpr int RB = 128;                               // code bytes per row per k-slice
+constexpr int TILE = BM * RB;                         // one operand's slice in LDS (32 KB)
+constexpr int SLOT = 2 * TILE;                        // one LDS slot: A then B
+constexpr int DMA_W = TILE / 1024 / 4;                // 1 KB loads per wave per operand per slice
 constexpr unsigned OOB = 0x80000000u;                 // a buffer offset past every record
 constexpr int RSRC_FLAGS = 0x00020000;                // raw 32-bit buffer
 static_assert(BM == BN && BM == GT, "one thread per row stages the row-major scales");
 
 template <int FMT>
 struct GemmShape {
-  static constexpr int BK = FMT == 0 ? 128 : 64;     // k per slice
+  static constexpr int BK = FMT == 0 ? 256 : 128;    // k per slice
   static constexpr int NS = BK / 64;                 // k-steps per slice
   static constexpr int NG = BK / 32;                 // scale groups per slice
 };
@@ -74,23 +74,23 @@ static __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p
 // not turn "load at (c ? offset : OOB)" back into a branch around two loads.
 static __device__ __forceinline__ void opaque_offset(unsigned &off) { asm volatile("" : "+v"(off)); }
 
-// Scale layouts: SL 0 row-major bytes; SL 1 blocked (a lane's word for its
-// 32-row block and 256-deep k-span is one coalesced 32-bit load); SL 2
-// row-major with groups % NG == 0, so a thread's NG bytes of a slice are one
-// aligned load.
+// Scale layouts: SL 0 row-major bytes; SL 1 blocked (a wave's words for its
+// 8 tiles and one 256-deep k-span are two 1 KB loads straight into LDS);
+// SL 2 row-major with groups % NG == 0, so a row's NG bytes of a slice are
+// one aligned load.
 template <int FMT, int OUT, int SL, bool TAIL>
 __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                                                  const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
                                                  int64_t M, int64_t N, int64_t K, float alpha,
                                                  void *__restrict__ C) {
   using S = GemmShape<FMT>;
-  constexpr int BK = S::BK, NG = S::NG;
+  constexpr int BK = S::BK, NS = S::NS, NG = S::NG;
   constexpr int CBSZ = FMT == 0 ? 4 : 0;  // FP4 E2M1 : FP8 E4M3
-  constexpr int NW = SL == 1 ? 4 : 2 * (BM + BN);  // row-major scale words per ring slot
-  __shared__ __attribute__((aligned(16))) uint8_t sm[NBUF * BUF];
-  __shared__ __attribute__((aligned(16))) unsigned ssw[NBUF][NW];
-  // blocked scale words of two 256-deep k-spans, per wave (SL 1)
-  __shared__ __attribute__((aligned(16))) unsigned wsl[SL == 1 ? 2 : 1][4][TI + TJ][64];
+  constexpr int NWB = SL == 1 ? 4 * (TI + TJ) * 64 : 4;   // blocked words per slot
+  constexpr int NWR = SL == 1 ? 4 : 2 * (BM + BN);        // row-major words per slot
+  __shared__ __attribute__((aligned(1024))) uint8_t sm0[SLOT], sm1[SLOT];
+  __shared__ __attribute__((aligned(1024))) unsigned wb0[NWB], wb1[NWB];
+  __shared__ __attribute__((aligned(16))) unsigned wr0[NWR], wr1[NWR];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -117,137 +117,123 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
     rBs = make_rsrc(Bs + n0 * groups, (uint32_t)nrows * (uint32_t)groups);
   }
 
-  // this thread's chunks: rows tid/4 + 64 it, logical chunk tid%4, stored at
-  // physical chunk (tid%4) ^ ((row/4)%4) = (tid%4) ^ ((tid/16)%4)
-  const int crow = tid >> 2, cchunk = tid & 3;
-  const int wr_off = crow * RB + 16 * (cchunk ^ ((tid >> 4) & 3));
-  // fragment read offsets: row r of a 32-row tile, logical chunk c at c ^ ((r/4)%4)
-  const int sw = (r >> 2) & 3;
-  int rd_off[2];
-  if constexpr (FMT == 0) {
-    rd_off[0] = r * RB + 16 * ((0 + h) ^ sw);  // k-step 0: chunk h
-    rd_off[1] = r * RB + 16 * ((2 + h) ^ sw);  // k-step 1: chunk 2 + h
-  } else {
-    rd_off[0] = r * RB + 16 * ((0 + h) ^ sw);  // bytes [16h, 16h + 16) of group 0
-    rd_off[1] = r * RB + 16 * ((2 + h) ^ sw);  // and of group 1
-  }
-  auto tile_off = [&](int f) { return f < TI ? (wm + 32 * f) * RB : TILE + (wn + 32 * (f - TI)) * RB; };
-
-  // ---- staged registers: two sets (slice parity) ------------------------------
-  // Scale words: SL 0 and 2 stage, per row, the slice's groups split into an
-  // even word (groups 0, 2) and an odd word (groups 1, 3), so that a lane of
-  // half h finds its k-step s scale in byte s of word h.  SL 1 words (byte t
-  // = k-step t of a 256-deep span) change once per span and have their own
-  // pipeline below.
-  constexpr int NSW = SL == 1 ? 1 : 4;
-  struct Staged {
-    u32x4 a[CPT], b[CPT];
-    unsigned w[NSW];
-  };
-  Staged st[2];
-
-  // row offsets of this thread's chunks; the slice offset goes in the
-  // instruction's scalar offset.  Prefetches past the last slice re-read the
-  // last slice (their data is never used), so no load leaves the operands.
-  unsigned rowoff[CPT];
+  // ---- code loads: wave load i of an operand fills 1 KB of LDS, rows
+  // 8g..8g+7 (g = 4i + wave); lane L takes row 8g + L/8 and physical chunk
+  // L%8, which holds logical chunk (L%8) ^ ((row/2)%8) ------------------------
+  unsigned dvoff[DMA_W];
+  int dchunk[DMA_W];
 #pragma unroll
-  for (int it = 0; it < CPT; ++it) rowoff[it] = (unsigned)((crow + 64 * it) * rb + 16 * cchunk);
-  auto load_slice = [&](Staged &s, int ks) {
+  for (int i = 0; i < DMA_W; ++i) {
+    const int row = 8 * (4 * i + wave) + (lane >> 3);
+    dchunk[i] = (lane & 7) ^ ((row >> 1) & 7);
+    dvoff[i] = (unsigned)(row * rb + 16 * dchunk[i]);
+  }
+  auto slot_of = [&](auto Pc) -> uint8_t * { return decltype(Pc)::value ? sm1 : sm0; };
+  // load slice ks into slot P (prefetches past the last slice re-read it)
+  auto load_slice = [&](auto Pc, int ks) {
+    uint8_t *slot = slot_of(Pc);
     const int kq = ks < nslices ? ks : nslices - 1;
     const int kb0 = kq * RB;
-    unsigned voff[CPT];
 #pragma unroll
-    for (int it = 0; it < CPT; ++it) {
-      voff[it] = rowoff[it];
+    for (int i = 0; i < DMA_W; ++i) {
+      unsigned off = dvoff[i];
       if constexpr (TAIL) {
         // the last slice of a K that is not a whole number of slices:
         // chunks past the row read as zero
-        voff[it] = 16 * cchunk < rb - kb0 ? voff[it] : OOB;
-        opaque_offset(voff[it]);
+        off = 16 * dchunk[i] < rb - kb0 ? off : OOB;
+        opaque_offset(off);
       }
+      uint8_t *dst = slot + (4 * i + wave) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, MX_LDS(dst), 16, off, kb0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, MX_LDS(dst + TILE), 16, off, kb0, 0, 0);
     }
-#pragma unroll
-    for (int it = 0; it < CPT; ++it) {
-      s.a[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, (int)voff[it], kb0, 0));
-      s.b[it] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, (int)voff[it], kb0, 0));
-    }
-    if constexpr (SL != 1) {
-      unsigned wa, wb;
-      if constexpr (SL == 2) {
-        // NG aligned bytes per row
-        if constexpr (NG == 4) {
-          wa = __builtin_amdgcn_raw_buffer_load_b32(rAs, tid * groups, kq * NG, 0);
-          wb = __builtin_amdgcn_raw_buffer_load_b32(rBs, tid * groups, kq * NG, 0);
-        } else {
-          wa = __builtin_amdgcn_raw_buffer_load_b16(rAs, tid * groups, kq * NG, 0);
-          wb = __builtin_amdgcn_raw_buffer_load_b16(rBs, tid * groups, kq * NG, 0);
-        }
-      } else {
-        // bytes; groups past K re-read the row's last group, whose codes
-        // there are zero
-        wa = wb = 0;
-#pragma unroll
-        for (int j = 0; j < NG; ++j) {
-          const int g = kq * NG + j < groups ? kq * NG + j : groups - 1;
-          wa |= (unsigned)__builtin_amdgcn_raw_buffer_load_b8(rAs, tid * groups, g, 0) << (8 * j);
-          wb |= (unsigned)__builtin_amdgcn_raw_buffer_load_b8(rBs, tid * groups, g, 0) << (8 * j);
-        }
-      }
-      // even and odd groups: bytes (0, 2) and (1, 3)
-      s.w[0] = __builtin_amdgcn_perm(0u, wa, 0x0c0c0200u);
-      s.w[1] = __builtin_amdgcn_perm(0u, wa, 0x0c0c0301u);
-      s.w[2] = __builtin_amdgcn_perm(0u, wb, 0x0c0c0200u);
-      s.w[3] = __builtin_amdgcn_perm(0u, wb, 0x0c0c0301u);
-    }
-  };
-  auto store_slice = [&](const Staged &s, int buf) {
-    uint8_t *base = sm + buf * BUF + wr_off;
-#pragma unroll
-    for (int it = 0; it < CPT; ++it) {
-      *(u32x4 *)(base + it * 64 * RB) = s.a[it];
-      *(u32x4 *)(base + TILE + it * 64 * RB) = s.b[it];
-    }
-    if constexpr (SL != 1) {
-      *(uint2 *)&ssw[buf][2 * tid] = uint2{s.w[0], s.w[1]};
-      *(uint2 *)&ssw[buf][2 * (BM + tid)] = uint2{s.w[2], s.w[3]};
+    if constexpr (SL == 1) {
+      // blocked words of the slice's 256-deep span: lane L takes words
+      // 4(L%16)..4(L%16)+3 of tile L/16 (A tiles, then B tiles)
+      unsigned *wb = decltype(Pc)::value ? wb1 : wb0;
+      const int span = (kq * BK) >> 8;
+      const unsigned va = (unsigned)(((wm >> 5) + (lane >> 4)) * gblocks * 256 + 16 * (lane & 15));
+      const unsigned vb = (unsigned)(((wn >> 5) + (lane >> 4)) * gblocks * 256 + 16 * (lane & 15));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, MX_LDS(wb + wave * (TI + TJ) * 64), 16, va, span * 256, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, MX_LDS(wb + (wave * (TI + TJ) + TI) * 64), 16, vb, span * 256,
+                                               0, 0);
     }
   };
 
-  // Blocked scale words, once per 256-deep k-span: a wave's 8 tiles x 64
-  // words of a span are two 16-byte loads per lane (lane L: tile L/16 of the
-  // A or B half, words 4(L%16)..4(L%16)+3), staged in registers one span
-  // ahead and written to a per-wave LDS slot, from which lane l reads word l
-  // of each tile.  Only the wave itself touches its slots, so program order
-  // is the only ordering needed.
-  u32x4 wst[2];
-  auto load_span_words = [&](int span) {
-    const int sp = span < gblocks ? span : gblocks - 1;
-    const unsigned va = (unsigned)(((wm >> 5) + (lane >> 4)) * gblocks * 256 + 16 * (lane & 15));
-    const unsigned vb = (unsigned)(((wn >> 5) + (lane >> 4)) * gblocks * 256 + 16 * (lane & 15));
-    wst[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rAs, (int)va, sp * 256, 0));
-    wst[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rBs, (int)vb, sp * 256, 0));
+  // ---- row-major scales (SL 0, 2): a thread loads its A row's and B row's
+  // NG bytes of a slice and stores them split by group parity: word h holds
+  // groups h, 2+h, 4+h, 6+h, so byte t is the scale of k-step t for lanes of
+  // half h ------------------------------------------------------------------
+  struct RowScales {
+    u32x2 a, b;
   };
-  auto store_span_words = [&](int span) {
-    uint8_t *base = (uint8_t *)&wsl[span & 1][wave][0][0] + 16 * lane;
-    *(u32x4 *)base = wst[0];
-    *(u32x4 *)(base + 4 * 64 * 4) = wst[1];
+  auto load_row_scales = [&](int ks) -> RowScales {
+    const int kq = ks < nslices ? ks : nslices - 1;
+    RowScales v{};
+    if constexpr (SL == 2) {
+      if constexpr (NG == 8) {
+        v.a = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rAs, tid * groups, kq * NG, 0));
+        v.b = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rBs, tid * groups, kq * NG, 0));
+      } else {
+        v.a.x = __builtin_amdgcn_raw_buffer_load_b32(rAs, tid * groups, kq * NG, 0);
+        v.b.x = __builtin_amdgcn_raw_buffer_load_b32(rBs, tid * groups, kq * NG, 0);
+      }
+    } else if constexpr (SL == 0) {
+      // bytes; groups past K re-read the row's last group, whose codes there
+      // are zero
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const int g = kq * NG + j < groups ? kq * NG + j : groups - 1;
+        const unsigned ba = __builtin_amdgcn_raw_buffer_load_b8(rAs, tid * groups, g, 0);
+        const unsigned bb = __builtin_amdgcn_raw_buffer_load_b8(rBs, tid * groups, g, 0);
+        if (j < 4) {
+          v.a.x |= ba << (8 * j);
+          v.b.x |= bb << (8 * j);
+        } else {
+          v.a.y |= ba << (8 * (j - 4));
+          v.b.y |= bb << (8 * (j - 4));
+        }
+      }
+    }
+    return v;
+  };
+  auto store_row_scales = [&](auto Pc, const RowScales &v) {
+    unsigned *wr = decltype(Pc)::value ? wr1 : wr0;
+    *(u32x2 *)&wr[2 * tid] = u32x2{__builtin_amdgcn_perm(v.a.y, v.a.x, 0x06040200u),
+                                   __builtin_amdgcn_perm(v.a.y, v.a.x, 0x07050301u)};
+    *(u32x2 *)&wr[2 * (BM + tid)] = u32x2{__builtin_amdgcn_perm(v.b.y, v.b.x, 0x06040200u),
+                                          __builtin_amdgcn_perm(v.b.y, v.b.x, 0x07050301u)};
   };
 
   // ---- fragments and scale words ---------------------------------------------
+  // lane offsets: row r of a 32-row tile, logical chunk c at c ^ ((r/2)%8)
+  const int sw = (r >> 1) & 7;
+  int rd[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    // E2M1: k-step t is chunk 2t + h; E4M3: k-step t/2's chunk 4(t/2) + 2(t%2) + h
+    const int c = FMT == 0 ? 2 * t + h : 4 * (t >> 1) + 2 * (t & 1) + h;
+    rd[t] = r * RB + 16 * (c ^ sw);
+  }
   using Frag = typename std::conditional<FMT == 0, u32x4, i32x8>::type;
-  auto read_frag = [&](int buf, int f, int s) -> Frag {
-    const uint8_t *p = sm + buf * BUF + tile_off(f);
+  auto tile_off = [&](int f) { return f < TI ? (wm + 32 * f) * RB : TILE + (wn + 32 * (f - TI)) * RB; };
+  auto read_frag = [&](auto Pc, int f, int t) -> Frag {
+    const uint8_t *p = slot_of(Pc) + tile_off(f);
     if constexpr (FMT == 0) {
-      return *(const u32x4 *)(p + rd_off[s]);
+      return *(const u32x4 *)(p + rd[t]);
     } else {
-      const u32x4 lo = *(const u32x4 *)(p + rd_off[0]), hi = *(const u32x4 *)(p + rd_off[1]);
+      const u32x4 lo = *(const u32x4 *)(p + rd[2 * t]), hi = *(const u32x4 *)(p + rd[2 * t + 1]);
       return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
   };
-  // scale word of tile f for slice ks (ring slot buf)
-  auto read_word = [&](int buf, int ks, int f) -> unsigned {
-    if constexpr (SL == 1) return wsl[((ks * BK) >> 8) & 1][wave][f][lane];
-    else return ssw[buf][2 * (f < TI ? wm + 32 * f + r : BM + wn + 32 * (f - TI) + r) + h];
+  auto read_word = [&](auto Pc, int f) -> unsigned {
+    if constexpr (SL == 1) {
+      const unsigned *wb = decltype(Pc)::value ? wb1 : wb0;
+      return wb[(wave * (TI + TJ) + f) * 64 + lane];
+    } else {
+      const unsigned *wr = decltype(Pc)::value ? wr1 : wr0;
+      return wr[2 * (f < TI ? wm + 32 * f + r : BM + wn + 32 * (f - TI) + r) + h];
+    }
   };
 
   f32x16 acc[TI][TJ];
@@ -256,14 +242,15 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
 
-  // 16 MFMAs of one k-step; the scale byte is picked by the instruction's
-  // byte select (BYTE)
-  auto mfma = [&](auto BYTE, const Frag *fr, const unsigned *w) {
+  // MFMAs [lo, hi) of one k-step's 16 (row-major over the 4 x 4 tiles); the
+  // scale byte is picked by the instruction's byte select (BYTE)
+  auto mfma = [&](auto BYTE, const Frag *fr, const unsigned *w, int lo = 0, int hi = TI * TJ) {
     constexpr int byte = decltype(BYTE)::value;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
+        if (TJ * i + j < lo || TJ * i + j >= hi) continue;
         i32x8 fa, fb;
         if constexpr (FMT == 0) {
           const u32x4 a = fr[i], b = fr[TI + j];  // upper halves unused for E2M1
@@ -277,119 +264,82 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
                                                                     (int)w[i], byte, (int)w[TI + j]);
       }
   };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
 
   // fragments of the next k-step to run, and the scale words of its slice
   Frag fr[2][TI + TJ];
   unsigned wd[TI + TJ];
 
   if (nslices > 0) {
-    if constexpr (SL == 1) {
-      load_span_words(0);
-      store_span_words(0);
-      load_span_words(1);
-    }
-    load_slice(st[0], 0);
-    store_slice(st[0], 0);
-    load_slice(st[1], 1);
-    store_slice(st[1], 1);
-    load_slice(st[0], 2);
-    load_slice(st[1], 3);
+    load_slice(P0{}, 0);
+    if constexpr (SL != 1) store_row_scales(P0{}, load_row_scales(0));
     __syncthreads();
 #pragma unroll
     for (int f = 0; f < TI + TJ; ++f) {
-      fr[0][f] = read_frag(0, f, 0);
-      wd[f] = read_word(0, 0, f);
+      fr[0][f] = read_frag(P0{}, f, 0);
+      wd[f] = read_word(P0{}, f);
     }
   }
 
-  // one k-slice: ks in ring slot b0, at position Q of its 256-deep k-span
-  // (slices start a span at Q = 0); the staged set Q%2 holds slice ks+2 and
-  // is refilled with slice ks+4
-  auto slice = [&](auto Qc, int ks, int b0) {
-    constexpr int q = decltype(Qc)::value, p = q & 1;
-    const int b1 = b0 == NBUF - 1 ? 0 : b0 + 1, b2 = b1 == NBUF - 1 ? 0 : b1 + 1;
-    if constexpr (FMT == 0) {
-      // k-step 0; read k-step 1's fragments and stage slice ks+2
-      mfma(std::integral_constant<int, SL == 1 ? 2 * q : 0>{}, fr[0], wd);
+  // one k-slice ks in slot P (P = ks % 2)
+  auto slice = [&](auto Pc, int ks) {
+    constexpr int P = decltype(Pc)::value;
+    using Q = std::integral_constant<int, P ^ 1>;
+    // scale byte of k-step t: blocked E4M3 slices are half a span
+    auto byte_of = [](auto T) { return std::integral_constant<int, (SL == 1 && FMT == 1 ? 2 * P : 0) + decltype(T)::value>{}; };
+    load_slice(Q{}, ks + 1);
+    RowScales rs{};
+    if constexpr (SL != 1) rs = load_row_scales(ks + 1);
+    // k-steps 0..NS-2, each reading the next step's fragments
+    auto step = [&](auto T) {
+      constexpr int t = decltype(T)::value;
+      mfma(byte_of(T), fr[t & 1], wd);
 #pragma unroll
-      for (int f = 0; f < TI + TJ; ++f) fr[1][f] = read_frag(b0, f, 1);
-      store_slice(st[p], b2);
-      if constexpr (SL == 1 && q == 0) {
-        // the next span's words to LDS, the one after into registers
-        store_span_words(((ks * BK) >> 8) + 1);
-        load_span_words(((ks * BK) >> 8) + 2);
-      }
+      for (int f = 0; f < TI + TJ; ++f) fr[(t + 1) & 1][f] = read_frag(Pc, f, t + 1);
 #pragma unroll
       for (int k = 0; k < TI * TJ; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        if (k < TI + TJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // fragment read
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+        if (t == 0) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // loads of the next slice
+        __builtin_amdgcn_sched_group_barrier(0x100, FMT == 0 ? 1 : 2, 0);  // fragment reads
       }
-      // k-step 1; load slice ks+4, read slice ks+1's first fragments
-      unsigned wcur[TI + TJ];
-#pragma unroll
-      for (int f = 0; f < TI + TJ; ++f) wcur[f] = wd[f];
-      mfma(std::integral_constant<int, SL == 1 ? 2 * q + 1 : 1>{}, fr[1], wcur);
-      load_slice(st[p], ks + 4);
-#pragma unroll
-      for (int f = 0; f < TI + TJ; ++f) {
-        fr[0][f] = read_frag(b1, f, 0);
-        wd[f] = read_word(b1, ks + 1, f);
-      }
-#pragma unroll
-      for (int k = 0; k < TI * TJ; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      }
-    } else {
-      // the slice's one k-step; stage slice ks+2, load slice ks+4, read
-      // slice ks+1's fragments into the other set
-      unsigned wcur[TI + TJ];
-#pragma unroll
-      for (int f = 0; f < TI + TJ; ++f) wcur[f] = wd[f];
-      mfma(std::integral_constant<int, SL == 1 ? q : 0>{}, fr[p], wcur);
-      store_slice(st[p], b2);
-      if constexpr (SL == 1 && q == 0) {
-        store_span_words(((ks * BK) >> 8) + 1);
-        load_span_words(((ks * BK) >> 8) + 2);
-      }
-      load_slice(st[p], ks + 4);
-#pragma unroll
-      for (int f = 0; f < TI + TJ; ++f) {
-        fr[p ^ 1][f] = read_frag(b1, f, 0);
-        wd[f] = read_word(b1, ks + 1, f);
-      }
-#pragma unroll
-      for (int k = 0; k < TI * TJ; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-      }
+    };
+    step(std::integral_constant<int, 0>{});
+    if constexpr (NS == 4) {
+      step(std::integral_constant<int, 1>{});
+      step(std::integral_constant<int, 2>{});
     }
+    if constexpr (SL != 1) store_row_scales(Q{}, rs);
+    // The last k-step: most of its MFMAs, then the barrier that publishes
+    // the next slice (once every wave's loads have landed: the later the
+    // barrier, the longer the loads have), then the rest of the MFMAs
+    // overlapping the reads of the next slice's first fragments.
+    constexpr int AFTER = 8;  // enough MFMA time to cover the reads
+    unsigned wcur[TI + TJ];
+#pragma unroll
+    for (int f = 0; f < TI + TJ; ++f) wcur[f] = wd[f];
+    const auto last = byte_of(std::integral_constant<int, NS - 1>{});
+    mfma(last, fr[(NS - 1) & 1], wcur, 0, TI * TJ - AFTER);
     __syncthreads();
-    return b1;
+    mfma(last, fr[(NS - 1) & 1], wcur, TI * TJ - AFTER, TI * TJ);
+#pragma unroll
+    for (int f = 0; f < TI + TJ; ++f) {
+      fr[0][f] = read_frag(Q{}, f, 0);
+      wd[f] = read_word(Q{}, f);
+    }
+#pragma unroll
+    for (int k = 0; k < AFTER; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TI + TJ) / AFTER * (FMT == 0 ? 1 : 2), 0);  // LDS reads
+    }
   };
 
-  // slices per 256-deep k-span: the loop runs whole spans, so that every
-  // scale byte select is a constant
-  constexpr int U = 256 / BK;
-  int ks = 0, b0 = 0;
-  for (; ks + U <= nslices; ks += U) {
-    b0 = slice(std::integral_constant<int, 0>{}, ks, b0);
-    b0 = slice(std::integral_constant<int, 1>{}, ks + 1, b0);
-    if constexpr (U == 4) {
-      b0 = slice(std::integral_constant<int, 2>{}, ks + 2, b0);
-      b0 = slice(std::integral_constant<int, 3>{}, ks + 3, b0);
-    }
+  int ks = 0;
+  for (; ks + 1 < nslices; ks += 2) {
+    slice(P0{}, ks);
+    slice(P1{}, ks + 1);
   }
-  // the last, partial span
-  if (ks < nslices) b0 = slice(std::integral_constant<int, 0>{}, ks, b0);
-  if (ks + 1 < nslices) b0 = slice(std::integral_constant<int, 1>{}, ks + 1, b0);
-  if constexpr (U == 4) {
-    if (ks + 2 < nslices) b0 = slice(std::integral_constant<int, 2>{}, ks + 2, b0);
-  }
+  if (ks < nslices) slice(P0{}, ks);
 
   // accumulator: lane l, register a holds C[8(a/4) + 4(l/32) + a%4][l%32]
 #pragma unroll
@@ -435,9 +385,9 @@ hipError_t launch_gemm(int fmt, const uint8_t *a, const uint8_t *as, const uint8
   if (scale_layout == 1) {
     run_gemm_k<1>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
   } else {
-    // whole-word row-major scale loads when every slice's groups are aligned
-    const int ng = fmt == 0 ? 4 : 2;
-    const bool aligned = (K / 32) % ng == 0 && (uintptr_t)as % ng == 0 && (uintptr_t)bs % ng == 0;
+    // one aligned load per row and slice when every slice's groups line up
+    const int ng = fmt == 0 ? GemmShape<0>::NG : GemmShape<1>::NG;
+    const bool aligned = (K / 32) % ng == 0 && (uintptr_t)as % 4 == 0 && (uintptr_t)bs % 4 == 0;
     if (aligned) run_gemm_k<2>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
     else run_gemm_k<0>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
   }
