@@ -70,10 +70,6 @@ static __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, RSRC_FLAGS);
 }
 
-// Keeps a selected buffer offset a plain value, so that the compiler does
-// not turn "load at (c ? offset : OOB)" back into a branch around two loads.
-static __device__ __forceinline__ void opaque_offset(unsigned &off) { asm volatile("" : "+v"(off)); }
-
 // Scale layouts: SL 0 row-major bytes; SL 1 blocked (a wave's words for its
 // 8 tiles and one 256-deep k-span are two 1 KB loads straight into LDS);
 // SL 2 row-major with groups % NG == 0, so a row's NG bytes of a slice are

@@ -217,6 +217,11 @@ __device__ __forceinline__ unsigned nv_bf16_pair(unsigned c, float kf) {
 // to 8; 256-byte blocks of 32 rows x 8 groups in row-major block order; word
 // l of a block holds row l%32 and, in bytes 0..3, groups h, 2+h, 4+h, 6+h of
 // the block (h = l/32); padding bytes are 127 (2^0).
+// Keeps a selected buffer offset a plain value, so that the compiler does
+// not turn "access at (c ? offset : out-of-range)" back into a branch around
+// two accesses.
+__device__ __forceinline__ void opaque_offset(unsigned &off) { asm volatile("" : "+v"(off)); }
+
 struct BlockedScales {
   int64_t rows, groups, gblocks;  // M, K/32, ceil(K/32 / 8)
 };
