@@ -266,10 +266,15 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   // fragments of the next k-step to run, and the scale words of its slice
   Frag fr[2][TI + TJ];
   unsigned wd[TI + TJ];
+  RowScales rs_next{};  // row-major scales of the slice after next (SL 0, 2)
 
   if (nslices > 0) {
     load_slice(P0{}, 0);
-    if constexpr (SL != 1) store_row_scales(P0{}, load_row_scales(0));
+    load_slice(P1{}, 1);
+    if constexpr (SL != 1) {
+      store_row_scales(P0{}, load_row_scales(0));
+      rs_next = load_row_scales(1);
+    }
     __syncthreads();
 #pragma unroll
     for (int f = 0; f < TI + TJ; ++f) {
@@ -284,9 +289,6 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
     using Q = std::integral_constant<int, P ^ 1>;
     // scale byte of k-step t: blocked E4M3 slices are half a span
     auto byte_of = [](auto T) { return std::integral_constant<int, (SL == 1 && FMT == 1 ? 2 * P : 0) + decltype(T)::value>{}; };
-    load_slice(Q{}, ks + 1);
-    RowScales rs{};
-    if constexpr (SL != 1) rs = load_row_scales(ks + 1);
     // k-steps 0..NS-2, each reading the next step's fragments
     auto step = [&](auto T) {
       constexpr int t = decltype(T)::value;
@@ -296,7 +298,6 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
 #pragma unroll
       for (int k = 0; k < TI * TJ; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        if (t == 0) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // loads of the next slice
         __builtin_amdgcn_sched_group_barrier(0x100, FMT == 0 ? 1 : 2, 0);  // fragment reads
       }
     };
@@ -305,11 +306,12 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       step(std::integral_constant<int, 1>{});
       step(std::integral_constant<int, 2>{});
     }
-    if constexpr (SL != 1) store_row_scales(Q{}, rs);
+    if constexpr (SL != 1) store_row_scales(Q{}, rs_next);
     // The last k-step: most of its MFMAs, then the barrier that publishes
-    // the next slice (once every wave's loads have landed: the later the
-    // barrier, the longer the loads have), then the rest of the MFMAs
-    // overlapping the reads of the next slice's first fragments.
+    // the next slice (once every wave's loads have landed) and frees this
+    // slice's slot, then the rest of the MFMAs overlapping the reads of the
+    // next slice's first fragments and the loads of the slice after next
+    // into this slot: those loads get a whole slice to land.
     constexpr int AFTER = 8;  // enough MFMA time to cover the reads
     unsigned wcur[TI + TJ];
 #pragma unroll
@@ -323,10 +325,13 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       fr[0][f] = read_frag(Q{}, f, 0);
       wd[f] = read_word(Q{}, f);
     }
+    load_slice(Pc, ks + 2);
+    if constexpr (SL != 1) rs_next = load_row_scales(ks + 2);
 #pragma unroll
     for (int k = 0; k < AFTER; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TI + TJ) / AFTER * (FMT == 0 ? 1 : 2), 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x010, 3, 0);  // loads of the slice after next
     }
   };
 
@@ -336,6 +341,9 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
     slice(P1{}, ks + 1);
   }
   if (ks < nslices) slice(P0{}, ks);
+  // the last slice's prefetch (a re-read of the last slice, never used) is
+  // still landing in LDS: drain it before the workgroup can end
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   // accumulator: lane l, register a holds C[8(a/4) + 4(l/32) + a%4][l%32]
 #pragma unroll
