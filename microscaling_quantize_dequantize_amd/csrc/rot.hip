@@ -375,6 +375,307 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// RB = 128 on 16-block tiles (4 KiB per wave) with v_mfma_f32_16x16x32_bf16.
+//
+// Streaming whole 8 KiB tiles per wave (32 blocks, the 32x32 layout above)
+// is slower on this GPU than 4 KiB ones: a persistent copy with the same
+// sweep runs at 5.8 TB/s with 8 KiB per wave and 6.1 TB/s with 4 KiB.  The
+// 16x16x32 MFMA needs only 16 blocks per tile.  Y^T = Reff^T . X^T with
+// m = output j (16 per jt, 8 jt), k = t (32 per kb, 4 kb), n = block:
+//   lane l = 16p + n;  B fragment kb: x[block n][t = 32kb + 8p + i];
+//   A fragment (jt, kb): Reff[32kb + 8p + i][16jt + n], i = 0..7;
+//   accumulator jt: y[block n][j = 16jt + 4p + i], i = 0..3.
+// The 32-group g is jt 2g and 2g+1: lane l holds its elements 4p..4p+3
+// ("run a") and 16+4p..16+4p+3 ("run b"), and the group spans lanes n,
+// n+16, n+32, n+48 (two lane swaps reduce the abs-max).  NVFP4 16-groups
+// are single jt.
+// LDS: a tile is 16 blocks x 16 pieces of 16 bytes; piece c of block n sits
+// at slot 16n + (c ^ n), so the fragment reads (16 lanes, one block each,
+// same c) and the coalesced accesses (16 lanes, one block's 16 pieces) are
+// both free of bank conflicts.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int slot16(int n, int c) { return 16 * n + (c ^ n); }
+
+// Max of v over lanes l, l^16, l^32 and l^48.
+__device__ __forceinline__ unsigned max_across_quarters(unsigned v) {
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max_across_halves(umax(r[0], r[1]));
+}
+
+// The MX step of one 32-group in the 16x16 layout: scale byte, scale
+// operand and the codes of run a and run b (E2M1: 16 bits, E4M3: 32 bits).
+template <int FMT>
+__device__ __forceinline__ void group16_codes(const f32x4 &a, const f32x4 &b, unsigned &sb, float &sc,
+                                              unsigned &ca, unsigned &cb) {
+  unsigned m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = umax(m, __float_as_uint(a[i]) & 0x7FFFFFFFu);
+    m = umax(m, __float_as_uint(b[i]) & 0x7FFFFFFFu);
+  }
+  m = max_across_quarters(m);
+  sb = scale_byte<FMT>(m);
+  sc = scale_operand(sb);
+  float ya[4], yb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ya[i] = a[i];
+    yb[i] = b[i];
+  }
+  if (FMT == 1) {
+    const float cl = __uint_as_float(((sb + 8u) << 23) | 0x600000u);  // 448 * 2^s
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ya[i] = clamp_f32(ya[i], cl);
+      yb[i] = clamp_f32(yb[i], cl);
+    }
+  }
+  if (FMT == 0) {
+    ca = fp4_from_f32x2<1>(fp4_from_f32x2<0>(0u, ya[0], ya[1], sc), ya[2], ya[3], sc);
+    cb = fp4_from_f32x2<1>(fp4_from_f32x2<0>(0u, yb[0], yb[1], sc), yb[2], yb[3], sc);
+  } else {
+    ca = fp8_from_f32x2<true>(fp8_from_f32x2<false>(0u, ya[0], ya[1], sc), ya[2], ya[3], sc);
+    cb = fp8_from_f32x2<true>(fp8_from_f32x2<false>(0u, yb[0], yb[1], sc), yb[2], yb[3], sc);
+  }
+}
+
+// bf16 of a run's 4 codes (8 bytes): E2M1 16 bits or E4M3 32 bits.
+template <int FMT>
+__device__ __forceinline__ u32x2 run_bf16(unsigned c, float sc) {
+  if (FMT == 0)
+    return u32x2{__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 0)),
+                 __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 1))};
+  return u32x2{__builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, sc, false)),
+               __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, sc, true))};
+}
+
+// NVFP4 16-group (one jt) in the 16x16 layout: scale byte and value, and
+// the E2M1 codes of this lane's 4 elements (16 bits).
+__device__ __forceinline__ void nv_group16(const f32x4 &a, float g, float c6, unsigned &sb, float &sbv,
+                                           unsigned &c) {
+  unsigned m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = umax(m, __float_as_uint(a[i]) & 0x7FFFFFFFu);
+  m = max_across_quarters(m);
+  sb = nv_scale_byte(__uint_as_float(m) * c6);
+  sbv = nv_scale_value(sb);
+  const float mul = sbv == 0.0f ? 0.0f : g / sbv;
+  c = fp4_from_f32x2<1>(fp4_from_f32x2<0>(0u, a[0] * mul, a[1] * mul, 1.0f), a[2] * mul, a[3] * mul, 1.0f);
+}
+
+// (T16_WAVES_PER_SIMD workgroup-waves share each SIMD: the register budget
+// the compiler schedules for)
+constexpr int T16_WAVES_PER_SIMD = 3;
+
+template <int FMT, int OP, int THREADS, int SL>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(T16_WAVES_PER_SIMD)))
+void k_rot128_t16(const uint16_t *__restrict__ src,
+                                                        const uint16_t *__restrict__ rot, int r,
+                                                        void *__restrict__ dst, uint8_t *__restrict__ codes,
+                                                        uint8_t *__restrict__ scales, int64_t n_blk,
+                                                        BlockedScales bl, const float *__restrict__ gp) {
+  constexpr int RB = 128, NJT = 8, NKB = 4, TB = 16;  // 16-wide j tiles, 32-deep k steps, blocks per tile
+  constexpr bool FP4 = FMT != 1;
+  constexpr int TP = TB * 16;                       // 16-byte input pieces per tile
+  constexpr int NL = TP / 64;                       // coalesced pieces per lane
+  constexpr int WAVES = THREADS / 64;
+  __shared__ u32x4 sA[NJT * NKB * 64];
+  __shared__ u32x4 sT[WAVES][TP];
+
+  // R is staged in the A-fragment buffer itself (RB*RB*2 bytes = its size),
+  // then the fragments are built in the tile buffers and copied back.
+  static_assert(sizeof(sA) == RB * RB * 2 && sizeof(sT) >= 0, "R staging");
+  {
+    constexpr int RP = (RB * RB / 8 + THREADS - 1) / THREADS;
+    const int pieces = r * r / 8;
+    u32x4 rv[RP];
+#pragma unroll
+    for (int k = 0; k < RP; ++k) {
+      const int i = threadIdx.x + k * THREADS;
+      if (i < pieces) rv[k] = ((const u32x4 *)rot)[i];
+    }
+#pragma unroll
+    for (int k = 0; k < RP; ++k) {
+      const int i = threadIdx.x + k * THREADS;
+      if (i < pieces) sA[i] = rv[k];
+    }
+  }
+  __syncthreads();
+  if (SL == 1)
+    write_blocked_pads(scales, bl, (int64_t)blockIdx.x * THREADS + threadIdx.x, (int64_t)gridDim.x * THREADS);
+  // A fragment (jt, kb) of lane ln: Reff[32kb + 8(ln/16) + i][16jt + ln%16],
+  // gathered from R in sA into registers, then written over sA after a
+  // barrier
+  constexpr int FPT = (NJT * NKB * 64 + THREADS - 1) / THREADS;  // fragments per thread
+  u32x4 fa[FPT];
+  {
+    const uint16_t *Rs = (const uint16_t *)sA;
+#pragma unroll
+    for (int k = 0; k < FPT; ++k) {
+      const int idx = threadIdx.x + k * THREADS;
+      if (idx < NJT * NKB * 64) {
+        const int ln = idx & 63, f = idx >> 6, jt = f / NKB, kb = f % NKB;
+        const int j = jt * 16 + (ln & 15), t0 = 32 * kb + 8 * (ln >> 4);
+        unsigned w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = (unsigned)reff(Rs, r, t0 + 2 * i, j) | ((unsigned)reff(Rs, r, t0 + 2 * i + 1, j) << 16);
+        fa[k] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < FPT; ++k) {
+    const int idx = threadIdx.x + k * THREADS;
+    if (idx < NJT * NKB * 64) sA[idx] = fa[k];
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, p = lane >> 4, n = lane & 15;
+  u32x4 *T = sT[threadIdx.x >> 6];
+  float g = 0.0f, c6 = 0.0f;
+  if constexpr (FMT == 2) {
+    g = *gp;
+    c6 = g / 6.0f;
+  }
+  const int64_t n_elem = n_blk * RB;
+  const int64_t n_tiles = (n_blk + TB - 1) / TB;
+  const int64_t stride = (int64_t)gridDim.x * WAVES;
+
+  // coalesced loads of one tile: lane piece 64q + lane (block (64q+lane)/16)
+  auto load_tile = [&](int64_t tile, u32x4 *v) {
+    const int64_t e_tile = tile * TB * RB;
+    const u32x4 *gs = (const u32x4 *)(src + e_tile) + lane;
+    if (e_tile + (int64_t)TP * 8 <= n_elem) {
+#pragma unroll
+      for (int q = 0; q < NL; ++q) v[q] = __builtin_nontemporal_load(gs + q * 64);
+    } else {
+#pragma unroll
+      for (int q = 0; q < NL; ++q)
+        v[q] = e_tile + (int64_t)(q * 64 + lane) * 8 < n_elem ? __builtin_nontemporal_load(gs + q * 64)
+                                                             : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  int64_t tile = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
+  u32x4 v[NL];
+  if (tile < n_tiles) load_tile(tile, v);
+  for (; tile < n_tiles; tile += stride) {
+    const int64_t e_tile = tile * TB * RB;
+    const bool full = e_tile + (int64_t)TP * 8 <= n_elem;
+    // 1. the tile into LDS (piece P = 64q + lane is block P/16, piece P%16)
+#pragma unroll
+    for (int q = 0; q < NL; ++q) T[slot16(4 * q + p, n)] = v[q];
+    wave_lds_sync();
+    // 2. B fragments: block n, pieces 4kb + p
+    u32x4 b[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) b[kb] = T[slot16(n, 4 * kb + p)];
+    wave_lds_sync();
+    // 3. rotate and quantize, one 32-group (jt 2g, 2g+1) at a time
+    const int64_t blk = tile * TB + n;
+    uint64_t sbw = 0;
+#pragma unroll
+    for (int gq = 0; gq < NJT / 2; ++gq) {
+      f32x4 acc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          acc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, sA[((2 * gq + hh) * NKB + kb) * 64 + lane]),
+              __builtin_bit_cast(bf16x8, b[kb]), acc[hh], 0, 0, 0);
+      if constexpr (FMT == 2) {
+        unsigned sb[2], c[2];
+        float sbv[2];
+        nv_group16(acc[0], g, c6, sb[0], sbv[0], c[0]);
+        nv_group16(acc[1], g, c6, sb[1], sbv[1], c[1]);
+        sbw |= (uint64_t)(sb[0] | (sb[1] << 8)) << (16 * gq);
+        if (OP == OP_QDQ) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const float kf = sbv[hh] / g;
+            const u32x2 o{nv_bf16_pair<0>(c[hh], kf), nv_bf16_pair<1>(c[hh], kf)};
+            ((u32x2 *)T)[2 * slot16(n, 4 * gq + 2 * hh + (p >> 1)) + (p & 1)] = o;
+          }
+        } else {
+          // codes of block n: 8 bytes per 16-group, this lane's 2 bytes at 2p
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            ((uint16_t *)T)[(n * 4 + gq) * 8 + 4 * hh + p] = (uint16_t)c[hh];
+        }
+      } else {
+        unsigned sb, ca, cb;
+        float sc;
+        group16_codes<FMT>(acc[0], acc[1], sb, sc, ca, cb);
+        sbw |= (uint64_t)sb << (8 * gq);
+        if (OP == OP_QDQ) {
+          u32x2 oa = run_bf16<FMT>(ca, sc), ob = run_bf16<FMT>(cb, sc);
+          if (sb == 255u) oa = ob = u32x2{BF16_NAN | (BF16_NAN << 16), BF16_NAN | (BF16_NAN << 16)};
+          // run a: elements 32gq + 4p.. = piece 4gq + p/2, half p%2; run b: 2 pieces on
+          ((u32x2 *)T)[2 * slot16(n, 4 * gq + (p >> 1)) + (p & 1)] = oa;
+          ((u32x2 *)T)[2 * slot16(n, 4 * gq + 2 + (p >> 1)) + (p & 1)] = ob;
+        } else if (FP4) {
+          if (sb == 255u) ca = cb = 0u;
+          // codes of block n, group gq: 16 bytes; run a at byte 2p, run b at 8 + 2p
+          ((uint16_t *)T)[(n * 4 + gq) * 8 + p] = (uint16_t)ca;
+          ((uint16_t *)T)[(n * 4 + gq) * 8 + 4 + p] = (uint16_t)cb;
+        } else {
+          if (sb == 255u) ca = cb = 0x7F7F7F7Fu;
+          // codes of block n: 32 bytes per group; run a at byte 32gq + 4p, run b 16 on
+          ((unsigned *)T)[(n * 8 + 2 * gq) * 4 + p] = ca;
+          ((unsigned *)T)[(n * 8 + 2 * gq + 1) * 4 + p] = cb;
+        }
+      }
+    }
+    // scale bytes of block n: lanes p == 0
+    if (OP == OP_QUANT && SL == 1 && p == 0 && blk < n_blk) {
+      const int64_t gf0 = blk * 4, i = gf0 / bl.groups, g0 = gf0 - i * bl.groups;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) scales[blocked_offset(i, g0 + gq, bl.gblocks)] = (uint8_t)(sbw >> (8 * gq));
+    } else if (OP == OP_QUANT && FMT == 2 && p == 0 && blk < n_blk) {
+      *(unsigned *)(scales + blk * 8) = (unsigned)sbw;
+      *(unsigned *)(scales + blk * 8 + 4) = (unsigned)(sbw >> 32);
+    } else if (OP == OP_QUANT && p == 0 && blk < n_blk) {
+      *(unsigned *)(scales + blk * 4) = (unsigned)sbw;
+    }
+    wave_lds_sync();
+    // 4. coalesced stores of the tile's outputs
+    if (OP == OP_QDQ) {
+      u32x4 *gd = (u32x4 *)((uint16_t *)dst + e_tile) + lane;
+      u32x4 o[NL];
+#pragma unroll
+      for (int q = 0; q < NL; ++q) o[q] = T[slot16(4 * q + p, n)];
+      if (full) {
+#pragma unroll
+        for (int q = 0; q < NL; ++q) __builtin_nontemporal_store(o[q], gd + q * 64);
+      } else {
+#pragma unroll
+        for (int q = 0; q < NL; ++q)
+          if (e_tile + (int64_t)(q * 64 + lane) * 8 < n_elem) __builtin_nontemporal_store(o[q], gd + q * 64);
+      }
+    } else {
+      // code pieces are stored linearly: block n's codes are pieces
+      // n*CP .. n*CP + CP - 1 (CP = 4 for E2M1, 8 for E4M3)
+      constexpr int CP = FP4 ? 4 : 8;
+      constexpr int EPP = FP4 ? 32 : 16;          // elements per code piece
+      constexpr int NQ = TB * CP / 64;
+      u32x4 *gd = (u32x4 *)(codes + e_tile / EPP * 16) + lane;
+      u32x4 o[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) o[q] = T[q * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if (full || e_tile + (int64_t)(q * 64 + lane) * EPP < n_elem) __builtin_nontemporal_store(o[q], gd + q * 64);
+    }
+    wave_lds_sync();
+    if (tile + stride < n_tiles) load_tile(tile + stride, v);
+  }
+}
+
 // The rotation alone (fp32 out) or fp32 sources: direct stores.
 // For bf16 sources the B layout is the one above; for fp32 sources
 // v_mfma_f32_32x32x2_f32 takes one value per lane: lane l supplies
@@ -509,11 +810,29 @@ static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
   return (unsigned)(g < cap ? g : cap);
 }
 
+// RB = 128 runs on 16-block tiles: T16_THREADS per workgroup, T16_PER_CU
+// resident per CU (LDS: 32 KiB of A fragments plus a 4 KiB tile per wave),
+// a persistent grid of exactly that many.
+constexpr int T16_THREADS = 256, T16_PER_CU = 3;
+
 template <int FMT, int OP, int RB>
 static void run_staged(const void *src, const void *rot, int r, void *dst, uint8_t *codes, uint8_t *scales,
                        int64_t n, hipStream_t st, const BlockedScales *bl, const float *gp = nullptr) {
   using Cfg = StagedCfg<RB>;
   const int64_t n_blk = n / RB;
+  if constexpr (RB == 128) {
+    const unsigned g = persistent_grid((n_blk + 15) / 16, T16_THREADS / 64, T16_PER_CU);
+    if constexpr (OP == OP_QUANT && FMT != 2) {
+      if (bl != nullptr) {
+        k_rot128_t16<FMT, OP, T16_THREADS, 1><<<g, T16_THREADS, 0, st>>>(
+            (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, *bl, nullptr);
+        return;
+      }
+    }
+    k_rot128_t16<FMT, OP, T16_THREADS, 0><<<g, T16_THREADS, 0, st>>>(
+        (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, BlockedScales{0, 0, 0}, gp);
+    return;
+  }
   const unsigned g = persistent_grid((n_blk + 31) / 32, Cfg::threads / 64, Cfg::per_cu);
   if constexpr (OP == OP_QUANT && FMT != 2) {
     if (bl != nullptr) {
