@@ -792,17 +792,16 @@ __global__ __launch_bounds__(DTHREADS) void k_rot_f32(const float *__restrict__ 
   }
 }
 
-// Launch shape of the staged kernels: workgroup size and workgroups per CU
-// in the grid.  LDS per workgroup is RB*RB*2 bytes of A fragments plus a
-// 64*RB-byte tile buffer per wave.  Chosen by measurement on MI355X (8192 x
-// 57344 bf16, QDQ and quantize).  For RB = 128 only two workgroups fit in a
-// CU's LDS, and a grid of exactly that many (persistent) is fastest: a grid
-// that is not a multiple of the resident count leaves a partial last round.
-// For RB = 64 a grid of 32 per CU (about 3.5 tiles per wave) is fastest.
+// Launch shape of the 32-block staged kernels (RB = 32, 64): workgroup
+// size and workgroups per CU in the grid.  LDS per workgroup is RB*RB*2
+// bytes of A fragments plus a 64*RB-byte tile buffer per wave.  Chosen by
+// measurement on MI355X (8192 x 57344 bf16, QDQ and quantize): for RB = 64
+// a grid of 32 per CU (about 3.5 tiles per wave) is fastest.  RB = 128 runs
+// on 16-block tiles (k_rot128_t16), persistent: a grid that is not a
+// multiple of the resident count leaves a partial last round.
 template <int RB> struct StagedCfg;
 template <> struct StagedCfg<32> { static constexpr int threads = 1024, per_cu = 8; };
 template <> struct StagedCfg<64> { static constexpr int threads = 512, per_cu = 32; };
-template <> struct StagedCfg<128> { static constexpr int threads = 256, per_cu = 2; };
 
 static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
   int64_t g = (tiles + waves - 1) / waves;
@@ -818,7 +817,6 @@ constexpr int T16_THREADS = 256, T16_PER_CU = 3;
 template <int FMT, int OP, int RB>
 static void run_staged(const void *src, const void *rot, int r, void *dst, uint8_t *codes, uint8_t *scales,
                        int64_t n, hipStream_t st, const BlockedScales *bl, const float *gp = nullptr) {
-  using Cfg = StagedCfg<RB>;
   const int64_t n_blk = n / RB;
   if constexpr (RB == 128) {
     const unsigned g = persistent_grid((n_blk + 15) / 16, T16_THREADS / 64, T16_PER_CU);
@@ -832,17 +830,19 @@ static void run_staged(const void *src, const void *rot, int r, void *dst, uint8
     k_rot128_t16<FMT, OP, T16_THREADS, 0><<<g, T16_THREADS, 0, st>>>(
         (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, BlockedScales{0, 0, 0}, gp);
     return;
-  }
-  const unsigned g = persistent_grid((n_blk + 31) / 32, Cfg::threads / 64, Cfg::per_cu);
-  if constexpr (OP == OP_QUANT && FMT != 2) {
-    if (bl != nullptr) {
-      k_rot_bf16<FMT, OP, RB, Cfg::threads, 1><<<g, Cfg::threads, 0, st>>>(
-          (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, *bl, nullptr);
-      return;
+  } else {
+    using Cfg = StagedCfg<RB>;
+    const unsigned g = persistent_grid((n_blk + 31) / 32, Cfg::threads / 64, Cfg::per_cu);
+    if constexpr (OP == OP_QUANT && FMT != 2) {
+      if (bl != nullptr) {
+        k_rot_bf16<FMT, OP, RB, Cfg::threads, 1><<<g, Cfg::threads, 0, st>>>(
+            (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, *bl, nullptr);
+        return;
+      }
     }
+    k_rot_bf16<FMT, OP, RB, Cfg::threads, 0><<<g, Cfg::threads, 0, st>>>(
+        (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, BlockedScales{0, 0, 0}, gp);
   }
-  k_rot_bf16<FMT, OP, RB, Cfg::threads, 0><<<g, Cfg::threads, 0, st>>>(
-      (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, BlockedScales{0, 0, 0}, gp);
 }
 
 template <int FMT, int OP, int RB>
