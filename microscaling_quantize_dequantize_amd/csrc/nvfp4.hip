@@ -46,10 +46,9 @@ static __device__ __forceinline__ u32x4 nv_bf16x8(unsigned c, float kf) {
   return u32x4{nv_bf16_pair<0>(c, kf), nv_bf16_pair<1>(c, kf), nv_bf16_pair<2>(c, kf), nv_bf16_pair<3>(c, kf)};
 }
 
-template <int OP>
-__global__ __launch_bounds__(NV_T) void k_nv_unrot(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
-                                                   uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
-                                                   const float *__restrict__ gp, int64_t n_pieces) {
+// QDQ: one lane per 16-byte piece, a lane pair per 16-group.
+__global__ __launch_bounds__(NV_T) void k_nv_qdq(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                                 const float *__restrict__ gp, int64_t n_pieces) {
   const float g = *gp;
   const float c6 = g / 6.0f;
   const int tid = threadIdx.x;
@@ -69,28 +68,43 @@ __global__ __launch_bounds__(NV_T) void k_nv_unrot(const u32x4 *__restrict__ src
     const unsigned sb = nv_scale_byte(amax * c6);
     const float sbv = nv_scale_value(sb);
     const float m = sbv == 0.0f ? 0.0f : g / sbv;
-    const unsigned c = nv_codes(w, m);
-    if (OP == OP_QDQ) {
-      const u32x4 o = nv_bf16x8(c, sbv / g);
-      if (p < n_pieces) __builtin_nontemporal_store(o, dst + p);
-    } else {
-      if (p < n_pieces) __builtin_nontemporal_store(c, (unsigned *)codes + p);
-      // scale bytes: lanes 8k..8k+7 hold 4 consecutive groups; gather the 4
-      // bytes into lane 8k (shifts within the 16-lane row, so that nothing
-      // wraps in from the other half) and store one word per 4 groups
-      unsigned v = sb << (8 * ((tid >> 1) & 3));
-      v |= dpp<DPP_ROW_SHL2>(v);
-      v |= dpp<DPP_ROW_SHL4>(v);
-      if ((tid & 7) == 0 && p < n_pieces) {
-        const int64_t g0 = p >> 1;
-        if (p + 8 <= n_pieces) {
-          *(unsigned *)(scales + g0) = v;
-        } else {
-          for (int k = 0; k < 4; ++k)
-            if (p + 2 * k < n_pieces) scales[g0 + k] = (uint8_t)(v >> (8 * k));
-        }
-      }
+    const u32x4 o = nv_bf16x8(nv_codes(w, m), sbv / g);
+    if (p < n_pieces) __builtin_nontemporal_store(o, dst + p);
+  }
+}
+
+// Quantize with one lane per 16-group (two 16-byte pieces): the scale, its
+// value and the division g / value are computed once per group instead of
+// by both lanes of a pair, and the abs-max needs no lane exchange (measured
+// 11% faster on the 8192 x 57344 layer).  QDQ stays on lane pairs: here its
+// output would be two 16-byte stores 32 bytes apart per lane, which measured
+// 6% slower than the pairs' contiguous stores.
+__global__ __launch_bounds__(NV_T) void k_nv_quant_g(const u32x4 *__restrict__ src, uint8_t *__restrict__ codes,
+                                                     uint8_t *__restrict__ scales, const float *__restrict__ gp,
+                                                     int64_t n_groups) {
+  const float g = *gp;
+  const float c6 = g / 6.0f;
+  const int64_t stride = (int64_t)gridDim.x * NV_T;
+  for (int64_t q = (int64_t)blockIdx.x * NV_T + threadIdx.x; q < n_groups; q += stride) {
+    const u32x4 w0 = __builtin_nontemporal_load(src + 2 * q), w1 = __builtin_nontemporal_load(src + 2 * q + 1);
+    unsigned mb;
+    {
+      u16x2 a = __builtin_bit_cast(u16x2, w0.x & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2, w0.y & 0x7FFF7FFFu);
+      u16x2 c = __builtin_bit_cast(u16x2, w0.z & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2, w0.w & 0x7FFF7FFFu);
+      u16x2 e = __builtin_bit_cast(u16x2, w1.x & 0x7FFF7FFFu), f = __builtin_bit_cast(u16x2, w1.y & 0x7FFF7FFFu);
+      u16x2 gg = __builtin_bit_cast(u16x2, w1.z & 0x7FFF7FFFu), hh = __builtin_bit_cast(u16x2, w1.w & 0x7FFF7FFFu);
+      u16x2 mm = __builtin_elementwise_max(__builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                                                     __builtin_elementwise_max(c, d)),
+                                           __builtin_elementwise_max(__builtin_elementwise_max(e, f),
+                                                                     __builtin_elementwise_max(gg, hh)));
+      mb = umax(mm[0], mm[1]);
     }
+    const float amax = __uint_as_float(mb << 16);
+    const unsigned sb = nv_scale_byte(amax * c6);
+    const float sbv = nv_scale_value(sb);
+    const float m = sbv == 0.0f ? 0.0f : g / sbv;
+    __builtin_nontemporal_store(u32x2{nv_codes(w0, m), nv_codes(w1, m)}, (u32x2 *)codes + q);
+    scales[q] = (uint8_t)sb;
   }
 }
 
@@ -124,11 +138,13 @@ static unsigned nv_grid(int64_t n_pieces) {
 
 hipError_t launch_nv_unrot(int op, const void *src, void *dst, uint8_t *codes, uint8_t *scales, const float *g,
                            int64_t n, hipStream_t stream) {
-  const int64_t np = n / 8;
-  if (op == OP_QDQ)
-    k_nv_unrot<OP_QDQ><<<nv_grid(np), NV_T, 0, stream>>>((const u32x4 *)src, (u32x4 *)dst, nullptr, nullptr, g, np);
-  else
-    k_nv_unrot<OP_QUANT><<<nv_grid(np), NV_T, 0, stream>>>((const u32x4 *)src, nullptr, codes, scales, g, np);
+  if (op == OP_QDQ) {
+    const int64_t np = n / 8;
+    k_nv_qdq<<<nv_grid(np), NV_T, 0, stream>>>((const u32x4 *)src, (u32x4 *)dst, g, np);
+  } else {
+    const int64_t ng = n / 16;
+    k_nv_quant_g<<<nv_grid(ng), NV_T, 0, stream>>>((const u32x4 *)src, codes, scales, g, ng);
+  }
   return hipGetLastError();
 }
 
