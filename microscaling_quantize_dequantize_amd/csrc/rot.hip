@@ -388,8 +388,7 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
 //   accumulator jt: y[block n][j = 16jt + 4p + i], i = 0..3.
 // The 32-group g is jt 2g and 2g+1: lane l holds its elements 4p..4p+3
 // ("run a") and 16+4p..16+4p+3 ("run b"), and the group spans lanes n,
-// n+16, n+32, n+48 (two lane swaps reduce the abs-max).  NVFP4 16-groups
-// are single jt.
+// n+16, n+32, n+48 (two lane swaps reduce the abs-max).  MX formats only.
 // LDS: a tile is 16 blocks x 16 pieces of 16 bytes; piece c of block n sits
 // at slot 16n + (c ^ n), so the fragment reads (16 lanes, one block each,
 // same c) and the coalesced accesses (16 lanes, one block's 16 pieces) are
@@ -451,20 +450,6 @@ __device__ __forceinline__ u32x2 run_bf16(unsigned c, float sc) {
                __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, sc, true))};
 }
 
-// NVFP4 16-group (one jt) in the 16x16 layout: scale byte and value, and
-// the E2M1 codes of this lane's 4 elements (16 bits).
-__device__ __forceinline__ void nv_group16(const f32x4 &a, float g, float c6, unsigned &sb, float &sbv,
-                                           unsigned &c) {
-  unsigned m = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m = umax(m, __float_as_uint(a[i]) & 0x7FFFFFFFu);
-  m = max_across_quarters(m);
-  sb = nv_scale_byte(__uint_as_float(m) * c6);
-  sbv = nv_scale_value(sb);
-  const float mul = sbv == 0.0f ? 0.0f : g / sbv;
-  c = fp4_from_f32x2<1>(fp4_from_f32x2<0>(0u, a[0] * mul, a[1] * mul, 1.0f), a[2] * mul, a[3] * mul, 1.0f);
-}
-
 // (T16_WAVES_PER_SIMD workgroup-waves share each SIMD: the register budget
 // the compiler schedules for)
 constexpr int T16_WAVES_PER_SIMD = 3;
@@ -476,8 +461,9 @@ void k_rot128_t16(const uint16_t *__restrict__ src,
                                                         void *__restrict__ dst, uint8_t *__restrict__ codes,
                                                         uint8_t *__restrict__ scales, int64_t n_blk,
                                                         BlockedScales bl, const float *__restrict__ gp) {
+  static_assert(FMT == 0 || FMT == 1, "MX formats");
   constexpr int RB = 128, NJT = 8, NKB = 4, TB = 16;  // 16-wide j tiles, 32-deep k steps, blocks per tile
-  constexpr bool FP4 = FMT != 1;
+  constexpr bool FP4 = FMT == 0;
   constexpr int TP = TB * 16;                       // 16-byte input pieces per tile
   constexpr int NL = TP / 64;                       // coalesced pieces per lane
   constexpr int WAVES = THREADS / 64;
@@ -536,11 +522,7 @@ void k_rot128_t16(const uint16_t *__restrict__ src,
 
   const int lane = threadIdx.x & 63, p = lane >> 4, n = lane & 15;
   u32x4 *T = sT[threadIdx.x >> 6];
-  float g = 0.0f, c6 = 0.0f;
-  if constexpr (FMT == 2) {
-    g = *gp;
-    c6 = g / 6.0f;
-  }
+  (void)gp;
   const int64_t n_elem = n_blk * RB;
   const int64_t n_tiles = (n_blk + TB - 1) / TB;
   const int64_t stride = (int64_t)gridDim.x * WAVES;
@@ -588,26 +570,7 @@ void k_rot128_t16(const uint16_t *__restrict__ src,
           acc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8, sA[((2 * gq + hh) * NKB + kb) * 64 + lane]),
               __builtin_bit_cast(bf16x8, b[kb]), acc[hh], 0, 0, 0);
-      if constexpr (FMT == 2) {
-        unsigned sb[2], c[2];
-        float sbv[2];
-        nv_group16(acc[0], g, c6, sb[0], sbv[0], c[0]);
-        nv_group16(acc[1], g, c6, sb[1], sbv[1], c[1]);
-        sbw |= (uint64_t)(sb[0] | (sb[1] << 8)) << (16 * gq);
-        if (OP == OP_QDQ) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const float kf = sbv[hh] / g;
-            const u32x2 o{nv_bf16_pair<0>(c[hh], kf), nv_bf16_pair<1>(c[hh], kf)};
-            ((u32x2 *)T)[2 * slot16(n, 4 * gq + 2 * hh + (p >> 1)) + (p & 1)] = o;
-          }
-        } else {
-          // codes of block n: 8 bytes per 16-group, this lane's 2 bytes at 2p
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-            ((uint16_t *)T)[(n * 4 + gq) * 8 + 4 * hh + p] = (uint16_t)c[hh];
-        }
-      } else {
+      {
         unsigned sb, ca, cb;
         float sc;
         group16_codes<FMT>(acc[0], acc[1], sb, sc, ca, cb);
@@ -636,9 +599,6 @@ void k_rot128_t16(const uint16_t *__restrict__ src,
       const int64_t gf0 = blk * 4, i = gf0 / bl.groups, g0 = gf0 - i * bl.groups;
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) scales[blocked_offset(i, g0 + gq, bl.gblocks)] = (uint8_t)(sbw >> (8 * gq));
-    } else if (OP == OP_QUANT && FMT == 2 && p == 0 && blk < n_blk) {
-      *(unsigned *)(scales + blk * 8) = (unsigned)sbw;
-      *(unsigned *)(scales + blk * 8 + 4) = (unsigned)(sbw >> 32);
     } else if (OP == OP_QUANT && p == 0 && blk < n_blk) {
       *(unsigned *)(scales + blk * 4) = (unsigned)sbw;
     }
@@ -792,16 +752,19 @@ __global__ __launch_bounds__(DTHREADS) void k_rot_f32(const float *__restrict__ 
   }
 }
 
-// Launch shape of the 32-block staged kernels (RB = 32, 64): workgroup
-// size and workgroups per CU in the grid.  LDS per workgroup is RB*RB*2
-// bytes of A fragments plus a 64*RB-byte tile buffer per wave.  Chosen by
-// measurement on MI355X (8192 x 57344 bf16, QDQ and quantize): for RB = 64
-// a grid of 32 per CU (about 3.5 tiles per wave) is fastest.  RB = 128 runs
-// on 16-block tiles (k_rot128_t16), persistent: a grid that is not a
-// multiple of the resident count leaves a partial last round.
+// Launch shape of the 32-block staged kernels: workgroup size and
+// workgroups per CU in the grid.  LDS per workgroup is RB*RB*2 bytes of A
+// fragments plus a 64*RB-byte tile buffer per wave.  Chosen by measurement
+// on MI355X (8192 x 57344 bf16, QDQ and quantize): for RB = 64 a grid of 32
+// per CU (about 3.5 tiles per wave) is fastest; for RB = 128 (used for
+// NVFP4) two workgroups fit in a CU's LDS and a persistent grid of exactly
+// that many is fastest (a grid that is not a multiple of the resident count
+// leaves a partial last round).  MX formats at RB = 128 run on 16-block
+// tiles (k_rot128_t16).
 template <int RB> struct StagedCfg;
 template <> struct StagedCfg<32> { static constexpr int threads = 1024, per_cu = 8; };
 template <> struct StagedCfg<64> { static constexpr int threads = 512, per_cu = 32; };
+template <> struct StagedCfg<128> { static constexpr int threads = 256, per_cu = 2; };
 
 static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
   int64_t g = (tiles + waves - 1) / waves;
@@ -809,16 +772,19 @@ static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
   return (unsigned)(g < cap ? g : cap);
 }
 
-// RB = 128 runs on 16-block tiles: T16_THREADS per workgroup, T16_PER_CU
-// resident per CU (LDS: 32 KiB of A fragments plus a 4 KiB tile per wave),
-// a persistent grid of exactly that many.
+// MX formats at RB = 128 run on 16-block tiles: T16_THREADS per workgroup,
+// T16_PER_CU resident per CU (LDS: 32 KiB of A fragments plus a 4 KiB tile
+// per wave), a persistent grid of exactly that many.  NVFP4 stays on
+// 32-block tiles: its 16-groups span four lanes here instead of two, so
+// each lane repeats the group's two correctly rounded divisions for twice
+// as many elements, and the VALU-bound NVFP4 path measured 15% slower.
 constexpr int T16_THREADS = 256, T16_PER_CU = 3;
 
 template <int FMT, int OP, int RB>
 static void run_staged(const void *src, const void *rot, int r, void *dst, uint8_t *codes, uint8_t *scales,
                        int64_t n, hipStream_t st, const BlockedScales *bl, const float *gp = nullptr) {
   const int64_t n_blk = n / RB;
-  if constexpr (RB == 128) {
+  if constexpr (RB == 128 && FMT != 2) {
     const unsigned g = persistent_grid((n_blk + 15) / 16, T16_THREADS / 64, T16_PER_CU);
     if constexpr (OP == OP_QUANT && FMT != 2) {
       if (bl != nullptr) {
