@@ -450,20 +450,19 @@ __device__ __forceinline__ u32x2 run_bf16(unsigned c, float sc) {
                __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, sc, true))};
 }
 
-// (T16_WAVES_PER_SIMD workgroup-waves share each SIMD: the register budget
-// the compiler schedules for)
-constexpr int T16_WAVES_PER_SIMD = 3;
+// T16_THREADS per workgroup, T16_PER_CU resident per CU (LDS: 32 KiB of A
+// fragments plus a 4 KiB tile per wave), so T16_WAVES_PER_SIMD waves share
+// each SIMD: the register budget the compiler schedules for.
+constexpr int T16_THREADS = 256, T16_PER_CU = 3, T16_WAVES_PER_SIMD = 3;
 
-template <int FMT, int OP, int THREADS, int SL>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(T16_WAVES_PER_SIMD)))
-void k_rot128_t16(const uint16_t *__restrict__ src,
-                                                        const uint16_t *__restrict__ rot, int r,
-                                                        void *__restrict__ dst, uint8_t *__restrict__ codes,
-                                                        uint8_t *__restrict__ scales, int64_t n_blk,
-                                                        BlockedScales bl, const float *__restrict__ gp) {
+// MX QDQ (bf16 in and out) with rotation 128 on 16-block tiles.
+template <int FMT>
+__global__ __launch_bounds__(T16_THREADS) __attribute__((amdgpu_waves_per_eu(T16_WAVES_PER_SIMD)))
+void k_rot128_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__ rot, int r,
+                  uint16_t *__restrict__ dst, int64_t n_blk) {
   static_assert(FMT == 0 || FMT == 1, "MX formats");
+  constexpr int THREADS = T16_THREADS;
   constexpr int RB = 128, NJT = 8, NKB = 4, TB = 16;  // 16-wide j tiles, 32-deep k steps, blocks per tile
-  constexpr bool FP4 = FMT == 0;
   constexpr int TP = TB * 16;                       // 16-byte input pieces per tile
   constexpr int NL = TP / 64;                       // coalesced pieces per lane
   constexpr int WAVES = THREADS / 64;
@@ -489,8 +488,6 @@ void k_rot128_t16(const uint16_t *__restrict__ src,
     }
   }
   __syncthreads();
-  if (SL == 1)
-    write_blocked_pads(scales, bl, (int64_t)blockIdx.x * THREADS + threadIdx.x, (int64_t)gridDim.x * THREADS);
   // A fragment (jt, kb) of lane ln: Reff[32kb + 8(ln/16) + i][16jt + ln%16],
   // gathered from R in sA into registers, then written over sA after a
   // barrier
@@ -522,7 +519,6 @@ void k_rot128_t16(const uint16_t *__restrict__ src,
 
   const int lane = threadIdx.x & 63, p = lane >> 4, n = lane & 15;
   u32x4 *T = sT[threadIdx.x >> 6];
-  (void)gp;
   const int64_t n_elem = n_blk * RB;
   const int64_t n_tiles = (n_blk + TB - 1) / TB;
   const int64_t stride = (int64_t)gridDim.x * WAVES;
@@ -557,9 +553,7 @@ void k_rot128_t16(const uint16_t *__restrict__ src,
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) b[kb] = T[slot16(n, 4 * kb + p)];
     wave_lds_sync();
-    // 3. rotate and quantize, one 32-group (jt 2g, 2g+1) at a time
-    const int64_t blk = tile * TB + n;
-    uint64_t sbw = 0;
+    // 3. rotate and QDQ, one 32-group (jt 2g, 2g+1) at a time
 #pragma unroll
     for (int gq = 0; gq < NJT / 2; ++gq) {
       f32x4 acc[2] = {f32x4{}, f32x4{}};
@@ -570,66 +564,28 @@ void k_rot128_t16(const uint16_t *__restrict__ src,
           acc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8, sA[((2 * gq + hh) * NKB + kb) * 64 + lane]),
               __builtin_bit_cast(bf16x8, b[kb]), acc[hh], 0, 0, 0);
-      {
-        unsigned sb, ca, cb;
-        float sc;
-        group16_codes<FMT>(acc[0], acc[1], sb, sc, ca, cb);
-        sbw |= (uint64_t)sb << (8 * gq);
-        if (OP == OP_QDQ) {
-          u32x2 oa = run_bf16<FMT>(ca, sc), ob = run_bf16<FMT>(cb, sc);
-          if (sb == 255u) oa = ob = u32x2{BF16_NAN | (BF16_NAN << 16), BF16_NAN | (BF16_NAN << 16)};
-          // run a: elements 32gq + 4p.. = piece 4gq + p/2, half p%2; run b: 2 pieces on
-          ((u32x2 *)T)[2 * slot16(n, 4 * gq + (p >> 1)) + (p & 1)] = oa;
-          ((u32x2 *)T)[2 * slot16(n, 4 * gq + 2 + (p >> 1)) + (p & 1)] = ob;
-        } else if (FP4) {
-          if (sb == 255u) ca = cb = 0u;
-          // codes of block n, group gq: 16 bytes; run a at byte 2p, run b at 8 + 2p
-          ((uint16_t *)T)[(n * 4 + gq) * 8 + p] = (uint16_t)ca;
-          ((uint16_t *)T)[(n * 4 + gq) * 8 + 4 + p] = (uint16_t)cb;
-        } else {
-          if (sb == 255u) ca = cb = 0x7F7F7F7Fu;
-          // codes of block n: 32 bytes per group; run a at byte 32gq + 4p, run b 16 on
-          ((unsigned *)T)[(n * 8 + 2 * gq) * 4 + p] = ca;
-          ((unsigned *)T)[(n * 8 + 2 * gq + 1) * 4 + p] = cb;
-        }
-      }
-    }
-    // scale bytes of block n: lanes p == 0
-    if (OP == OP_QUANT && SL == 1 && p == 0 && blk < n_blk) {
-      const int64_t gf0 = blk * 4, i = gf0 / bl.groups, g0 = gf0 - i * bl.groups;
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) scales[blocked_offset(i, g0 + gq, bl.gblocks)] = (uint8_t)(sbw >> (8 * gq));
-    } else if (OP == OP_QUANT && p == 0 && blk < n_blk) {
-      *(unsigned *)(scales + blk * 4) = (unsigned)sbw;
+      unsigned sb, ca, cb;
+      float sc;
+      group16_codes<FMT>(acc[0], acc[1], sb, sc, ca, cb);
+      u32x2 oa = run_bf16<FMT>(ca, sc), ob = run_bf16<FMT>(cb, sc);
+      if (sb == 255u) oa = ob = u32x2{BF16_NAN | (BF16_NAN << 16), BF16_NAN | (BF16_NAN << 16)};
+      // run a: elements 32gq + 4p.. = piece 4gq + p/2, half p%2; run b: 2 pieces on
+      ((u32x2 *)T)[2 * slot16(n, 4 * gq + (p >> 1)) + (p & 1)] = oa;
+      ((u32x2 *)T)[2 * slot16(n, 4 * gq + 2 + (p >> 1)) + (p & 1)] = ob;
     }
     wave_lds_sync();
     // 4. coalesced stores of the tile's outputs
-    if (OP == OP_QDQ) {
-      u32x4 *gd = (u32x4 *)((uint16_t *)dst + e_tile) + lane;
-      u32x4 o[NL];
+    u32x4 *gd = (u32x4 *)(dst + e_tile) + lane;
+    u32x4 o[NL];
 #pragma unroll
-      for (int q = 0; q < NL; ++q) o[q] = T[slot16(4 * q + p, n)];
-      if (full) {
+    for (int q = 0; q < NL; ++q) o[q] = T[slot16(4 * q + p, n)];
+    if (full) {
 #pragma unroll
-        for (int q = 0; q < NL; ++q) __builtin_nontemporal_store(o[q], gd + q * 64);
-      } else {
-#pragma unroll
-        for (int q = 0; q < NL; ++q)
-          if (e_tile + (int64_t)(q * 64 + lane) * 8 < n_elem) __builtin_nontemporal_store(o[q], gd + q * 64);
-      }
+      for (int q = 0; q < NL; ++q) __builtin_nontemporal_store(o[q], gd + q * 64);
     } else {
-      // code pieces are stored linearly: block n's codes are pieces
-      // n*CP .. n*CP + CP - 1 (CP = 4 for E2M1, 8 for E4M3)
-      constexpr int CP = FP4 ? 4 : 8;
-      constexpr int EPP = FP4 ? 32 : 16;          // elements per code piece
-      constexpr int NQ = TB * CP / 64;
-      u32x4 *gd = (u32x4 *)(codes + e_tile / EPP * 16) + lane;
-      u32x4 o[NQ];
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) o[q] = T[q * 64 + lane];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q)
-        if (full || e_tile + (int64_t)(q * 64 + lane) * EPP < n_elem) __builtin_nontemporal_store(o[q], gd + q * 64);
+      for (int q = 0; q < NL; ++q)
+        if (e_tile + (int64_t)(q * 64 + lane) * 8 < n_elem) __builtin_nontemporal_store(o[q], gd + q * 64);
     }
     wave_lds_sync();
     if (tile + stride < n_tiles) load_tile(tile + stride, v);
@@ -772,29 +728,21 @@ static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
   return (unsigned)(g < cap ? g : cap);
 }
 
-// MX formats at RB = 128 run on 16-block tiles: T16_THREADS per workgroup,
-// T16_PER_CU resident per CU (LDS: 32 KiB of A fragments plus a 4 KiB tile
-// per wave), a persistent grid of exactly that many.  NVFP4 stays on
-// 32-block tiles: its 16-groups span four lanes here instead of two, so
+// MX QDQ at RB = 128 runs on 16-block tiles (k_rot128_t16), a persistent
+// grid of T16_PER_CU workgroups per CU.  Quantize (whose outputs are a
+// quarter of QDQ's) measured as fast or faster on 32-block tiles, and NVFP4
+// stays there too: its 16-groups span four lanes here instead of two, so
 // each lane repeats the group's two correctly rounded divisions for twice
-// as many elements, and the VALU-bound NVFP4 path measured 15% slower.
-constexpr int T16_THREADS = 256, T16_PER_CU = 3;
+// as many elements (15% slower).
 
 template <int FMT, int OP, int RB>
 static void run_staged(const void *src, const void *rot, int r, void *dst, uint8_t *codes, uint8_t *scales,
                        int64_t n, hipStream_t st, const BlockedScales *bl, const float *gp = nullptr) {
   const int64_t n_blk = n / RB;
-  if constexpr (RB == 128 && FMT != 2) {
+  if constexpr (RB == 128 && FMT != 2 && OP == OP_QDQ) {
     const unsigned g = persistent_grid((n_blk + 15) / 16, T16_THREADS / 64, T16_PER_CU);
-    if constexpr (OP == OP_QUANT && FMT != 2) {
-      if (bl != nullptr) {
-        k_rot128_t16<FMT, OP, T16_THREADS, 1><<<g, T16_THREADS, 0, st>>>(
-            (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, *bl, nullptr);
-        return;
-      }
-    }
-    k_rot128_t16<FMT, OP, T16_THREADS, 0><<<g, T16_THREADS, 0, st>>>(
-        (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, BlockedScales{0, 0, 0}, gp);
+    k_rot128_t16<FMT><<<g, T16_THREADS, 0, st>>>((const uint16_t *)src, (const uint16_t *)rot, r,
+                                                 (uint16_t *)dst, n_blk);
     return;
   } else {
     using Cfg = StagedCfg<RB>;
