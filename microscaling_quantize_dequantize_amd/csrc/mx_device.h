@@ -203,6 +203,51 @@ __device__ __forceinline__ unsigned nv_scale_byte(float q) {
 // fp32 value of a (non-negative) E4M3 scale byte.
 __device__ __forceinline__ float nv_scale_value(unsigned sb) { return decode_mag<1>(sb, 0); }
 
+// The two per-group quotients of the NVFP4 steps, m = g / v and
+// kf = v / g (v the value of an E4M3 scale byte, g the per-tensor
+// multiplier), correctly rounded fp32 like a division, but without one
+// while g lies in [2^-60, 2^60] (nv_fast; outside it they divide):
+//  - v has at most 4 significant bits, so g / v is never halfway between two
+//    fp32 values and lies at least 1/30 ulp from every such midpoint; the
+//    Newton-corrected product q + (g - q v) rcp(v), q = g rcp(v), is within
+//    2^-16 ulp of g / v for any rcp within 2^-20 and rounds the same way;
+//  - v / g lies at least 2^-49 (relative) from every fp32 midpoint; the fp64
+//    product v * (1/g) (1/g correctly rounded in fp64) is within 2^-52 of it,
+//    so its conversion to fp32 is the correctly rounded quotient.
+// The same Newton form gives g / 6 (6 has 2 significant bits).  In range,
+// no intermediate overflows, underflows or goes subnormal.  The kernels
+// test the range once and run one of two instances of their loop.
+__device__ __forceinline__ bool nv_fast(float g) { return g >= 0x1p-60f && g <= 0x1p60f; }
+
+// g / d for d > 0 with at most 4 significant bits and g in range.
+__device__ __forceinline__ float nv_div_short(float g, float d) {
+  const float y = __builtin_amdgcn_rcpf(d);
+  const float q = g * y;
+  return __builtin_fmaf(__builtin_fmaf(-q, d, g), y, q);
+}
+
+struct NvTensor {
+  float g, c6;  // g and g / 6 (fp32, nearest-even)
+  double ig;    // 1 / g (fp64, nearest-even)
+};
+
+template <bool FAST>
+__device__ __forceinline__ NvTensor nv_tensor(float g) {
+  return NvTensor{g, FAST ? nv_div_short(g, 6.0f) : g / 6.0f, 1.0 / (double)g};
+}
+
+template <bool FAST>
+__device__ __forceinline__ float nv_mul(const NvTensor &t, float v) {
+  if (!FAST) return v == 0.0f ? 0.0f : t.g / v;
+  const float m = nv_div_short(t.g, v);
+  return v == 0.0f ? 0.0f : m;
+}
+
+template <bool FAST>
+__device__ __forceinline__ float nv_kf(const NvTensor &t, float v) {
+  return FAST ? (float)((double)v * t.ig) : v / t.g;
+}
+
 // Dequantized NVFP4 pair as packed bf16: E2M1 nibbles 2*BYTE and 2*BYTE+1
 // of the code word c (exact values from the hardware conversion with scale
 // 1), each times kf (fp32, nearest-even), then nearest-even to bf16.

@@ -34,6 +34,7 @@
 // of bank conflicts.
 #include "launch.h"
 #include "mx_device.h"
+#include <type_traits>
 
 namespace mx {
 
@@ -124,7 +125,8 @@ __device__ __forceinline__ void group_bf16(const unsigned c[4], unsigned sb, flo
 // lanes l and l+32) and j = 16-31 (acc[8..15]) are two 16-groups, each with
 // its own E4M3 scale byte (sb[0], sb[1]); the codes come out as for E2M1
 // (c[q]: 4 nibbles of elements 4q..4q+3 of this lane's run).
-__device__ __forceinline__ void nv_group_codes(const f32x16 &acc, float g, float c6, unsigned sb[2],
+template <bool FAST>
+__device__ __forceinline__ void nv_group_codes(const f32x16 &acc, const NvTensor &t, unsigned sb[2],
                                                float sbv[2], unsigned c[4]) {
 #pragma unroll
   for (int hg = 0; hg < 2; ++hg) {
@@ -132,10 +134,10 @@ __device__ __forceinline__ void nv_group_codes(const f32x16 &acc, float g, float
 #pragma unroll
     for (int a = 0; a < 8; ++a) m = umax(m, __float_as_uint(acc[8 * hg + a]) & 0x7FFFFFFFu);
     m = max_across_halves(m);
-    sb[hg] = nv_scale_byte(__uint_as_float(m) * c6);
+    sb[hg] = nv_scale_byte(__uint_as_float(m) * t.c6);
     sbv[hg] = nv_scale_value(sb[hg]);
   }
-  const float mul[2] = {sbv[0] == 0.0f ? 0.0f : g / sbv[0], sbv[1] == 0.0f ? 0.0f : g / sbv[1]};
+  const float mul[2] = {nv_mul<FAST>(t, sbv[0]), nv_mul<FAST>(t, sbv[1])};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const float mq = mul[q >> 1];
@@ -145,8 +147,10 @@ __device__ __forceinline__ void nv_group_codes(const f32x16 &acc, float g, float
 }
 
 // Dequantized bf16 of the two 16-groups of a tile, arranged as group_bf16.
-__device__ __forceinline__ void nv_group_bf16(const unsigned c[4], const float sbv[2], float g, unsigned o[8]) {
-  const float kf[2] = {sbv[0] / g, sbv[1] / g};
+template <bool FAST>
+__device__ __forceinline__ void nv_group_bf16(const unsigned c[4], const float sbv[2], const NvTensor &t,
+                                              unsigned o[8]) {
+  const float kf[2] = {nv_kf<FAST>(t, sbv[0]), nv_kf<FAST>(t, sbv[1])};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     o[2 * q] = nv_bf16_pair<0>(c[q], kf[q >> 1]);
@@ -189,12 +193,46 @@ __device__ __forceinline__ void group_fp8_bytes(const unsigned c[4], unsigned sb
 // FMT: 0 = MXFP4, 1 = MXFP8, 2 = NVFP4 (16-groups, E4M3 scales and the
 // per-tensor multiplier *gp).
 // SL (OP_QUANT only): 0 = row-major scales, 1 = the blocked layout `bl`.
-template <int FMT, int OP, int RB, int THREADS, int SL>
-__global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict__ src,
-                                                      const uint16_t *__restrict__ rot, int r,
-                                                      void *__restrict__ dst, uint8_t *__restrict__ codes,
-                                                      uint8_t *__restrict__ scales, int64_t n_blk,
-                                                      BlockedScales bl, const float *__restrict__ gp) {
+// Launch shape of the 32-block staged kernels (k_rot_bf16): workgroup size,
+// workgroups per CU in the grid (per_cu) and workgroups resident on a CU at
+// once (resident).  LDS per workgroup is RB*RB*2 bytes of A fragments plus a
+// 64*RB-byte tile buffer per wave; the launch pads it so that no more than
+// `resident` fit in a CU's LDS, and the kernel's register budget lets that
+// many fit (left to the register allocator, the residency changed from one
+// build to the next).  Chosen by measurement on MI355X (8192 x 57344 bf16,
+// QDQ and quantize): one resident workgroup (16 waves) for RB = 32 and two
+// (16 waves) for RB = 64 run 2-3% faster than the 32 and 24 waves that fit
+// otherwise.  For RB = 64 a grid of 32 per CU (about 3.5 tiles per wave) is
+// fastest; for RB = 128 (quantize and NVFP4) a persistent grid of exactly
+// the resident count (a grid that is not a multiple of it leaves a partial
+// last round).
+template <int RB> struct StagedCfg;
+template <> struct StagedCfg<32> { static constexpr int threads = 1024, per_cu = 8, resident = 1; };
+template <> struct StagedCfg<64> { static constexpr int threads = 512, per_cu = 32, resident = 2; };
+template <> struct StagedCfg<128> { static constexpr int threads = 256, per_cu = 2, resident = 2; };
+
+constexpr int LDS_PER_CU = 160 * 1024;
+
+// Static LDS of k_rot_bf16 at block size RB, and the dynamic LDS that the
+// launch adds so that at most StagedCfg<RB>::resident workgroups fit a CU.
+template <int RB> constexpr int staged_lds() {
+  return (RB / 32) * (RB / 16) * 64 * 16 + (StagedCfg<RB>::threads / 64) * (32 * RB / 8) * 16;
+}
+template <int RB> constexpr int staged_lds_pad() {
+  constexpr int need = LDS_PER_CU / (StagedCfg<RB>::resident + 1) + 1;
+  static_assert(StagedCfg<RB>::resident * (need > staged_lds<RB>() ? need : staged_lds<RB>()) + 1024 <= LDS_PER_CU,
+                "the resident workgroups fit");
+  return need > staged_lds<RB>() ? need - staged_lds<RB>() : 0;
+}
+
+// The tile loop of k_rot_bf16, once R's fragments are in sA: each wave
+// takes 32-block tiles (grid-stride), staging each through its LDS tile
+// buffer T.  NVFAST selects the division-free NVFP4 quotients (nv_mul).
+template <int FMT, int OP, int RB, int THREADS, int SL, bool NVFAST>
+__device__ __forceinline__ void rot_tiles(const uint16_t *__restrict__ src, void *__restrict__ dst,
+                                          uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                          int64_t n_blk, const BlockedScales &bl, float nv_g,
+                                          const u32x4 *sA, u32x4 *T) {
   constexpr int NJT = RB / 32, NKB = RB / 16;
   constexpr bool FP4 = FMT != 1;      // E2M1 codes (MXFP4 and NVFP4)
   constexpr int C = RB / 8;           // 16-byte input pieces per block
@@ -202,52 +240,7 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
   constexpr int WAVES = THREADS / 64;
   constexpr int C4 = RB / 32;         // E2M1 code pieces per block
   constexpr int C8 = RB / 16;         // E4M3 code pieces per block
-  __shared__ u32x4 sA[NJT * NKB * 64];
-  __shared__ u32x4 sT[WAVES][TP];
-
-  // R (r*r <= RB*RB bf16) is first copied into the tile buffers with
-  // coalesced 16-byte loads, all in flight at once; the fragments are then
-  // gathered from LDS.
-  static_assert(sizeof(sT) >= RB * RB * 2, "R is staged in the tile buffers");
-  {
-    constexpr int RP = (RB * RB / 8 + THREADS - 1) / THREADS;  // 16-byte pieces per thread
-    const int pieces = r * r / 8;
-    u32x4 rv[RP];
-#pragma unroll
-    for (int k = 0; k < RP; ++k) {
-      const int i = threadIdx.x + k * THREADS;
-      if (i < pieces) rv[k] = ((const u32x4 *)rot)[i];
-    }
-#pragma unroll
-    for (int k = 0; k < RP; ++k) {
-      const int i = threadIdx.x + k * THREADS;
-      if (i < pieces) (&sT[0][0])[i] = rv[k];
-    }
-  }
-  __syncthreads();
-  if (SL == 1)
-    write_blocked_pads(scales, bl, (int64_t)blockIdx.x * THREADS + threadIdx.x, (int64_t)gridDim.x * THREADS);
-  const uint16_t *Rs = (const uint16_t *)&sT[0][0];
-  // A fragment (jt, kb) of lane ln: Reff[t][j] for j = 32*jt + ln%32 and
-  // t = 16*kb + 8*(ln/32) + i, i = 0..7.
-  for (int idx = threadIdx.x; idx < NJT * NKB * 64; idx += THREADS) {
-    const int ln = idx & 63, f = idx >> 6, jt = f / NKB, kb = f % NKB;
-    const int j = jt * 32 + (ln & 31), t0 = 16 * kb + 8 * (ln >> 5);
-    unsigned w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = (unsigned)reff(Rs, r, t0 + 2 * i, j) | ((unsigned)reff(Rs, r, t0 + 2 * i + 1, j) << 16);
-    sA[idx] = u32x4{w[0], w[1], w[2], w[3]};
-  }
-  __syncthreads();
-
   const int lane = threadIdx.x & 63, h = lane >> 5, n = lane & 31;
-  u32x4 *T = sT[threadIdx.x >> 6];
-  float g = 0.0f, c6 = 0.0f;
-  if constexpr (FMT == 2) {
-    g = *gp;
-    c6 = g / 6.0f;
-  }
   const int64_t n_elem = n_blk * RB;
   const int64_t n_tiles = (n_blk + 31) / 32;
   const int64_t stride = (int64_t)gridDim.x * WAVES;
@@ -268,6 +261,8 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
     }
   };
 
+  NvTensor nvt{};
+  if constexpr (FMT == 2) nvt = nv_tensor<NVFAST>(nv_g);
   int64_t tile = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
   u32x4 v[NKB];
   if (tile < n_tiles) load_tile(tile, v);
@@ -300,10 +295,10 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
         if constexpr (FMT == 2) {
           unsigned sb2[2];
           float sbv[2];
-          nv_group_codes(acc, g, c6, sb2, sbv, c);
+          nv_group_codes<NVFAST>(acc, nvt, sb2, sbv, c);
           sb = 0u;  // never the NaN marker
           sbw |= (uint64_t)(sb2[0] | (sb2[1] << 8)) << (16 * jt);
-          if (OP == OP_QDQ) nv_group_bf16(c, sbv, g, o);
+          if (OP == OP_QDQ) nv_group_bf16<NVFAST>(c, sbv, nvt, o);
         } else {
           group_codes<FMT>(acc, sb, sc, c);
           sbw |= (uint64_t)sb << (8 * jt);
@@ -372,6 +367,67 @@ __global__ __launch_bounds__(THREADS) void k_rot_bf16(const uint16_t *__restrict
     }
     wave_lds_sync();
     if (tile + stride < n_tiles) load_tile(tile + stride, v);
+  }
+}
+
+template <int FMT, int OP, int RB, int THREADS, int SL>
+__global__ __launch_bounds__(THREADS)
+__attribute__((amdgpu_waves_per_eu(StagedCfg<RB>::resident * THREADS / 256))) void k_rot_bf16(const uint16_t *__restrict__ src,
+                                                      const uint16_t *__restrict__ rot, int r,
+                                                      void *__restrict__ dst, uint8_t *__restrict__ codes,
+                                                      uint8_t *__restrict__ scales, int64_t n_blk,
+                                                      BlockedScales bl, const float *__restrict__ gp) {
+  constexpr int NJT = RB / 32, NKB = RB / 16;
+  constexpr int TP = 32 * RB / 8;     // 16-byte input pieces per tile
+  constexpr int WAVES = THREADS / 64;
+  __shared__ u32x4 sA[NJT * NKB * 64];
+  __shared__ u32x4 sT[WAVES][TP];
+  static_assert(THREADS != StagedCfg<RB>::threads || sizeof(sA) + sizeof(sT) == staged_lds<RB>(), "LDS size");
+
+  // R (r*r <= RB*RB bf16) is first copied into the tile buffers with
+  // coalesced 16-byte loads, all in flight at once; the fragments are then
+  // gathered from LDS.
+  static_assert(sizeof(sT) >= RB * RB * 2, "R is staged in the tile buffers");
+  {
+    constexpr int RP = (RB * RB / 8 + THREADS - 1) / THREADS;  // 16-byte pieces per thread
+    const int pieces = r * r / 8;
+    u32x4 rv[RP];
+#pragma unroll
+    for (int k = 0; k < RP; ++k) {
+      const int i = threadIdx.x + k * THREADS;
+      if (i < pieces) rv[k] = ((const u32x4 *)rot)[i];
+    }
+#pragma unroll
+    for (int k = 0; k < RP; ++k) {
+      const int i = threadIdx.x + k * THREADS;
+      if (i < pieces) (&sT[0][0])[i] = rv[k];
+    }
+  }
+  __syncthreads();
+  if (SL == 1)
+    write_blocked_pads(scales, bl, (int64_t)blockIdx.x * THREADS + threadIdx.x, (int64_t)gridDim.x * THREADS);
+  const uint16_t *Rs = (const uint16_t *)&sT[0][0];
+  // A fragment (jt, kb) of lane ln: Reff[t][j] for j = 32*jt + ln%32 and
+  // t = 16*kb + 8*(ln/32) + i, i = 0..7.
+  for (int idx = threadIdx.x; idx < NJT * NKB * 64; idx += THREADS) {
+    const int ln = idx & 63, f = idx >> 6, jt = f / NKB, kb = f % NKB;
+    const int j = jt * 32 + (ln & 31), t0 = 16 * kb + 8 * (ln >> 5);
+    unsigned w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (unsigned)reff(Rs, r, t0 + 2 * i, j) | ((unsigned)reff(Rs, r, t0 + 2 * i + 1, j) << 16);
+    sA[idx] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+  __syncthreads();
+
+  u32x4 *T = sT[threadIdx.x >> 6];
+  if constexpr (FMT == 2) {
+    // one instance of the tile loop per range of g (see nv_mul)
+    const float g = *gp;
+    if (nv_fast(g)) rot_tiles<FMT, OP, RB, THREADS, SL, true>(src, dst, codes, scales, n_blk, bl, g, sA, T);
+    else rot_tiles<FMT, OP, RB, THREADS, SL, false>(src, dst, codes, scales, n_blk, bl, g, sA, T);
+  } else {
+    rot_tiles<FMT, OP, RB, THREADS, SL, true>(src, dst, codes, scales, n_blk, bl, 0.0f, sA, T);
   }
 }
 
@@ -708,19 +764,6 @@ __global__ __launch_bounds__(DTHREADS) void k_rot_f32(const float *__restrict__ 
   }
 }
 
-// Launch shape of the 32-block staged kernels: workgroup size and
-// workgroups per CU in the grid.  LDS per workgroup is RB*RB*2 bytes of A
-// fragments plus a 64*RB-byte tile buffer per wave.  Chosen by measurement
-// on MI355X (8192 x 57344 bf16, QDQ and quantize): for RB = 64 a grid of 32
-// per CU (about 3.5 tiles per wave) is fastest; for RB = 128 (used for
-// NVFP4) two workgroups fit in a CU's LDS and a persistent grid of exactly
-// that many is fastest (a grid that is not a multiple of the resident count
-// leaves a partial last round).  MX formats at RB = 128 run on 16-block
-// tiles (k_rot128_t16).
-template <int RB> struct StagedCfg;
-template <> struct StagedCfg<32> { static constexpr int threads = 1024, per_cu = 8; };
-template <> struct StagedCfg<64> { static constexpr int threads = 512, per_cu = 32; };
-template <> struct StagedCfg<128> { static constexpr int threads = 256, per_cu = 2; };
 
 static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
   int64_t g = (tiles + waves - 1) / waves;
@@ -732,8 +775,8 @@ static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
 // grid of T16_PER_CU workgroups per CU.  Quantize (whose outputs are a
 // quarter of QDQ's) measured as fast or faster on 32-block tiles, and NVFP4
 // stays there too: its 16-groups span four lanes here instead of two, so
-// each lane repeats the group's two correctly rounded divisions for twice
-// as many elements (15% slower).
+// each lane repeats the group's scale steps for twice as many elements
+// (measured 15% slower while those steps were divisions).
 
 template <int FMT, int OP, int RB>
 static void run_staged(const void *src, const void *rot, int r, void *dst, uint8_t *codes, uint8_t *scales,
@@ -749,12 +792,12 @@ static void run_staged(const void *src, const void *rot, int r, void *dst, uint8
     const unsigned g = persistent_grid((n_blk + 31) / 32, Cfg::threads / 64, Cfg::per_cu);
     if constexpr (OP == OP_QUANT && FMT != 2) {
       if (bl != nullptr) {
-        k_rot_bf16<FMT, OP, RB, Cfg::threads, 1><<<g, Cfg::threads, 0, st>>>(
+        k_rot_bf16<FMT, OP, RB, Cfg::threads, 1><<<g, Cfg::threads, staged_lds_pad<RB>(), st>>>(
             (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, *bl, nullptr);
         return;
       }
     }
-    k_rot_bf16<FMT, OP, RB, Cfg::threads, 0><<<g, Cfg::threads, 0, st>>>(
+    k_rot_bf16<FMT, OP, RB, Cfg::threads, 0><<<g, Cfg::threads, staged_lds_pad<RB>(), st>>>(
         (const uint16_t *)src, (const uint16_t *)rot, r, dst, codes, scales, n_blk, BlockedScales{0, 0, 0}, gp);
   }
 }

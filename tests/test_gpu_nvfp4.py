@@ -85,6 +85,17 @@ def test_unrotated_special_groups(mx):
         check_unrotated(mx, bits, g, f"special g={g}")
 
 
+@pytest.mark.parametrize("e", [60, -60, 61, -61, 100, -100])
+def test_unrotated_multiplier_range(mx, e):
+    """g = 2^e on both sides of the range in which the kernels form g / v
+    and v / g without a division, the input scaled by 2^-e so that the group
+    scales stay in range: bit-exact either way."""
+    M, K = 33, 160
+    x = W.random_bf16((M, K), seed=200 + e)
+    xs = W.f32_to_bf16_bits(W.bf16_bits_to_f32(x) * np.float32(2.0 ** -e))
+    check_unrotated(mx, xs, float(2.0 ** e), f"g=2^{e}")
+
+
 def test_unrotated_full_size(mx):
     """The 8192 x 28672 down-projection input (Student-t, nu = 3), the
     configuration the bench times: every code and scale byte bit-exact, and the
@@ -138,12 +149,19 @@ def test_rotated_full_size_sampled(mx):
     nv_band_check(y, beta, g, deq_gpu=qdq[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64))
 
 
-def test_identity_rotation_equals_unrotated(mx):
+@pytest.mark.parametrize("e", [None, 70, -70])
+def test_identity_rotation_equals_unrotated(mx, e):
+    """Rotation by the identity changes nothing, also for g outside the range
+    of the division-free quotients (g = 2^e, input scaled by 2^-e)."""
     import torch
     M, K = 64, 512
     x = W.random_bf16((M, K), seed=3)
     eye = W.f32_to_bf16_bits(np.eye(32, dtype=np.float32))
-    g = tensor_g(x)
+    if e is None:
+        g = tensor_g(x)
+    else:
+        x = W.f32_to_bf16_bits(W.bf16_bits_to_f32(x) * np.float32(2.0 ** -e))
+        g = float(2.0 ** e)
     xs = to_gpu_bf16(x)
     c1, s1 = mx.mx_nvfp4_quantize(xs, gscale(g), rot=to_gpu_bf16(eye))
     c0, s0 = mx.mx_nvfp4_quantize(xs, gscale(g))
