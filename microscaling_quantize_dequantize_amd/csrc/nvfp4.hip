@@ -131,25 +131,40 @@ __global__ __launch_bounds__(NV_T) void k_nv_quant_g(const u32x4 *__restrict__ s
   else nv_quant_loop<false>(src, codes, scales, nv_tensor<false>(g), n_groups);
 }
 
-template <int DT>
+// Dequantize: one lane per 8 elements, U pieces per lane (NV_T apart) whose
+// loads are issued together, as in the MX dequantize: two for bf16 output
+// (15% faster than one on the 8192 x 57344 layer), one for fp32 output
+// (two were 25% slower there).
+template <int DT, int U>
 __global__ __launch_bounds__(NV_T) void k_nv_dequant(const uint8_t *__restrict__ codes,
                                                      const uint8_t *__restrict__ scales,
                                                      const float *__restrict__ gp, void *__restrict__ dst,
                                                      int64_t n_pieces) {
+  constexpr int64_t SWEEP = NV_T * U;
   const float g = *gp;
-  const int64_t stride = (int64_t)gridDim.x * NV_T;
-  for (int64_t p = (int64_t)blockIdx.x * NV_T + threadIdx.x; p < n_pieces; p += stride) {
-    const float kf = nv_scale_value(scales[p >> 1]) / g;
-    const unsigned c = __builtin_nontemporal_load((const unsigned *)codes + p);
-    if (DT == 0) {
-      __builtin_nontemporal_store(nv_bf16x8(c, kf), (u32x4 *)dst + p);
-    } else {
-      unsigned v[8];
+  for (int64_t sweep = blockIdx.x; sweep * SWEEP < n_pieces; sweep += gridDim.x) {
+    unsigned sbs[U], cw[U];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = __float_as_uint(nv_value(c, k, kf));
-      u32x4 *d = (u32x4 *)dst + 2 * p;
-      __builtin_nontemporal_store(u32x4{v[0], v[1], v[2], v[3]}, d);
-      __builtin_nontemporal_store(u32x4{v[4], v[5], v[6], v[7]}, d + 1);
+    for (int u = 0; u < U; ++u) {
+      const int64_t p = sweep * SWEEP + u * NV_T + threadIdx.x;
+      sbs[u] = p < n_pieces ? scales[p >> 1] : 0u;
+      cw[u] = p < n_pieces ? __builtin_nontemporal_load((const unsigned *)codes + p) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t p = sweep * SWEEP + u * NV_T + threadIdx.x;
+      if (p >= n_pieces) continue;
+      const float kf = nv_scale_value(sbs[u]) / g;
+      if (DT == 0) {
+        __builtin_nontemporal_store(nv_bf16x8(cw[u], kf), (u32x4 *)dst + p);
+      } else {
+        unsigned v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = __float_as_uint(nv_value(cw[u], k, kf));
+        u32x4 *d = (u32x4 *)dst + 2 * p;
+        __builtin_nontemporal_store(u32x4{v[0], v[1], v[2], v[3]}, d);
+        __builtin_nontemporal_store(u32x4{v[4], v[5], v[6], v[7]}, d + 1);
+      }
     }
   }
 }
@@ -174,8 +189,8 @@ hipError_t launch_nv_unrot(int op, const void *src, void *dst, uint8_t *codes, u
 hipError_t launch_nv_dequant(int dtype, const uint8_t *codes, const uint8_t *scales, const float *g, void *dst,
                              int64_t n, hipStream_t stream) {
   const int64_t np = n / 8;
-  if (dtype == 0) k_nv_dequant<0><<<nv_grid(np), NV_T, 0, stream>>>(codes, scales, g, dst, np);
-  else k_nv_dequant<1><<<nv_grid(np), NV_T, 0, stream>>>(codes, scales, g, dst, np);
+  if (dtype == 0) k_nv_dequant<0, 2><<<nv_grid((np + 1) / 2), NV_T, 0, stream>>>(codes, scales, g, dst, np);
+  else k_nv_dequant<1, 1><<<nv_grid(np), NV_T, 0, stream>>>(codes, scales, g, dst, np);
   return hipGetLastError();
 }
 

@@ -167,44 +167,61 @@ __global__ __launch_bounds__(THREADS) void k_unrot_f32(const u32x4 *__restrict__
   }
 }
 
-// Dequantize: one lane per 8 elements (a quarter group).
-template <int FMT, int DT, int THREADS>
+// Dequantize: one lane per 8 elements (a quarter group), UNROLL pieces per
+// lane (THREADS apart) whose loads are issued together.  For bf16 output two
+// pieces measured 17% faster than one for MXFP4 on the 8192 x 57344 layer
+// (1% for MXFP8; four were slower); fp32 output, whose lanes already store
+// two 16-byte pieces each, stays at one.
+template <int FMT, int DT, int THREADS, int UNROLL>
 __global__ __launch_bounds__(THREADS) void k_dequant(const uint8_t *__restrict__ codes,
                                                      const uint8_t *__restrict__ scales,
                                                      void *__restrict__ dst, int64_t n_pieces) {
-  const int64_t stride = (int64_t)gridDim.x * THREADS;
-  for (int64_t p = (int64_t)blockIdx.x * THREADS + threadIdx.x; p < n_pieces; p += stride) {
-    const unsigned sb = scales[p >> 2];
-    const float sc = scale_operand(sb);
-    const int s = (int)sb - 127;
-    unsigned cw[2];
-    if (FMT == 0) {
-      cw[0] = __builtin_nontemporal_load((const unsigned *)codes + p);
-      cw[1] = 0u;
-    } else {
-      const u32x2 c = __builtin_nontemporal_load((const u32x2 *)codes + p);
-      cw[0] = c.x;
-      cw[1] = c.y;
-    }
-    if (DT == 0) {
-      u32x4 o = (FMT == 0) ? bf16x8_from_fp4(cw[0], sc) : bf16x8_from_fp8(u32x2{cw[0], cw[1]}, sc);
-      if (sb == 255u) {
-        const unsigned nn = BF16_NAN | (BF16_NAN << 16);
-        o = u32x4{nn, nn, nn, nn};
-      }
-      __builtin_nontemporal_store(o, (u32x4 *)dst + p);
-    } else {
-      constexpr int CB = FMT == 0 ? 4 : 8;
-      constexpr unsigned CM = (1u << CB) - 1u;
-      unsigned v[8];
+  constexpr int64_t SWEEP = THREADS * UNROLL;
+  for (int64_t sweep = blockIdx.x; sweep * SWEEP < n_pieces; sweep += gridDim.x) {
+    unsigned sbs[UNROLL], cw[UNROLL][2];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const unsigned code = (cw[(k * CB) / 32] >> ((k * CB) % 32)) & CM;
-        v[k] = sb == 255u ? F32_NAN : __float_as_uint(decode_code<FMT>(code, s));
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t p = sweep * SWEEP + u * THREADS + threadIdx.x;
+      sbs[u] = 0u;
+      cw[u][0] = cw[u][1] = 0u;
+      if (p < n_pieces) {
+        sbs[u] = scales[p >> 2];
+        if (FMT == 0) {
+          cw[u][0] = __builtin_nontemporal_load((const unsigned *)codes + p);
+        } else {
+          const u32x2 c = __builtin_nontemporal_load((const u32x2 *)codes + p);
+          cw[u][0] = c.x;
+          cw[u][1] = c.y;
+        }
       }
-      u32x4 *d = (u32x4 *)dst + 2 * p;
-      __builtin_nontemporal_store(u32x4{v[0], v[1], v[2], v[3]}, d);
-      __builtin_nontemporal_store(u32x4{v[4], v[5], v[6], v[7]}, d + 1);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t p = sweep * SWEEP + u * THREADS + threadIdx.x;
+      if (p >= n_pieces) continue;
+      const unsigned sb = sbs[u];
+      const float sc = scale_operand(sb);
+      const int s = (int)sb - 127;
+      if (DT == 0) {
+        u32x4 o = (FMT == 0) ? bf16x8_from_fp4(cw[u][0], sc) : bf16x8_from_fp8(u32x2{cw[u][0], cw[u][1]}, sc);
+        if (sb == 255u) {
+          const unsigned nn = BF16_NAN | (BF16_NAN << 16);
+          o = u32x4{nn, nn, nn, nn};
+        }
+        __builtin_nontemporal_store(o, (u32x4 *)dst + p);
+      } else {
+        constexpr int CB = FMT == 0 ? 4 : 8;
+        constexpr unsigned CM = (1u << CB) - 1u;
+        unsigned v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const unsigned code = (cw[u][(k * CB) / 32] >> ((k * CB) % 32)) & CM;
+          v[k] = sb == 255u ? F32_NAN : __float_as_uint(decode_code<FMT>(code, s));
+        }
+        u32x4 *d = (u32x4 *)dst + 2 * p;
+        __builtin_nontemporal_store(u32x4{v[0], v[1], v[2], v[3]}, d);
+        __builtin_nontemporal_store(u32x4{v[4], v[5], v[6], v[7]}, d + 1);
+      }
     }
   }
 }
@@ -218,6 +235,7 @@ static unsigned grid_for(int64_t n_pieces, int64_t per_block) {
 constexpr int QDQ_T = 128, QDQ_U = 1;
 constexpr int QNT_T = 128, QNT_U = 2;
 constexpr int DEQ_T = 128;
+template <int DT> constexpr int deq_unroll() { return DT == 0 ? 2 : 1; }
 
 hipError_t launch_unrot(int fmt, int op, int dtype, const void *src, void *dst, uint8_t *codes,
                         uint8_t *scales, int64_t n, hipStream_t stream, const BlockedScales *bl) {
@@ -256,13 +274,13 @@ hipError_t launch_unrot(int fmt, int op, int dtype, const void *src, void *dst, 
 hipError_t launch_dequant(int fmt, int dtype, const uint8_t *codes, const uint8_t *scales,
                           void *dst, int64_t n, hipStream_t stream) {
   const int64_t np = n / 8;
-  const unsigned g = grid_for(np, DEQ_T);
+  const unsigned g0 = grid_for(np, DEQ_T * deq_unroll<0>()), g1 = grid_for(np, DEQ_T * deq_unroll<1>());
   if (fmt == 0) {
-    if (dtype == 0) k_dequant<0, 0, DEQ_T><<<g, DEQ_T, 0, stream>>>(codes, scales, dst, np);
-    else k_dequant<0, 1, DEQ_T><<<g, DEQ_T, 0, stream>>>(codes, scales, dst, np);
+    if (dtype == 0) k_dequant<0, 0, DEQ_T, deq_unroll<0>()><<<g0, DEQ_T, 0, stream>>>(codes, scales, dst, np);
+    else k_dequant<0, 1, DEQ_T, deq_unroll<1>()><<<g1, DEQ_T, 0, stream>>>(codes, scales, dst, np);
   } else {
-    if (dtype == 0) k_dequant<1, 0, DEQ_T><<<g, DEQ_T, 0, stream>>>(codes, scales, dst, np);
-    else k_dequant<1, 1, DEQ_T><<<g, DEQ_T, 0, stream>>>(codes, scales, dst, np);
+    if (dtype == 0) k_dequant<1, 0, DEQ_T, deq_unroll<0>()><<<g0, DEQ_T, 0, stream>>>(codes, scales, dst, np);
+    else k_dequant<1, 1, DEQ_T, deq_unroll<1>()><<<g1, DEQ_T, 0, stream>>>(codes, scales, dst, np);
   }
   return hipGetLastError();
 }
