@@ -200,8 +200,12 @@ __device__ __forceinline__ unsigned nv_scale_byte(float q) {
   return fp8_from_f32x2<false>(0u, fminf(q, 448.0f), 0.0f, 1.0f) & 0xFFu;
 }
 
-// fp32 value of a (non-negative) E4M3 scale byte.
-__device__ __forceinline__ float nv_scale_value(unsigned sb) { return decode_mag<1>(sb, 0); }
+// fp32 value of an E4M3 scale byte: the hardware conversion (OCP E4M3:
+// sign, subnormals, NaN for 0x7F and 0xFF), exact.  The quantize paths only
+// produce bytes 0..0x7E; dequantize takes whatever bytes it is given.
+__device__ __forceinline__ float nv_scale_value(unsigned sb) {
+  return __builtin_amdgcn_cvt_scalef32_f32_fp8(sb, 1.0f, 0);
+}
 
 // The two per-group quotients of the NVFP4 steps, m = g / v and
 // kf = v / g (v the value of an E4M3 scale byte, g the per-tensor

@@ -96,6 +96,29 @@ def test_unrotated_multiplier_range(mx, e):
     check_unrotated(mx, xs, float(2.0 ** e), f"g=2^{e}")
 
 
+@pytest.mark.parametrize("g", [1.0, 2688.0, 2.0 ** 70])
+def test_dequantize_every_scale_byte(mx, g):
+    """Dequantize of every scale byte 0..255 (negative scales and the NaN
+    bytes 0x7F/0xFF included) with every E2M1 code: bit-exact against the
+    oracle's E4M3 decode where it gives a number, NaN where it gives NaN."""
+    import torch
+    K = 16 * 16
+    sb = np.arange(256, dtype=np.uint8).reshape(16, 16)   # 16 rows x 16 groups
+    nib = np.tile(np.arange(16, dtype=np.uint8), K // 16)
+    codes = np.tile((nib[0::2] | (nib[1::2] << 4))[None, :], (16, 1))
+    for dt, odt in ((torch.bfloat16, 0), (torch.float32, 1)):
+        d = mx.mx_nvfp4_dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(sb).cuda(), K, gscale(g),
+                                   dtype=dt)
+        torch.cuda.synchronize()
+        got = d.float().cpu().numpy()
+        want = oracle.nv_dequantize(codes, sb, K, g, dst_dtype=odt, threads=THREADS)
+        want_f = W.bf16_bits_to_f32(want) if odt == 0 else want.view(np.float32)
+        nan = np.isnan(want_f)
+        assert nan.sum() == 2 * 16, "the 0x7F and 0xFF groups"
+        assert np.array_equal(np.isnan(got), nan), f"NaN positions {dt}"
+        assert_bits_equal(bits_of(d)[~nan], want[~nan], f"every scale byte {dt} g={g}")
+
+
 def test_unrotated_full_size(mx):
     """The 8192 x 28672 down-projection input (Student-t, nu = 3), the
     configuration the bench times: every code and scale byte bit-exact, and the
