@@ -99,6 +99,30 @@ def reachable_domain_matrix(fmt):
 
 
 @pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_dequantize_every_code_and_scale(mx, fmt):
+    """Dequantize of every code (E2M1: 16, E4M3: 256, the NaN codes
+    included) under every scale byte 0..255 (255 = NaN), bf16 and fp32 out:
+    bit-exact against the oracle where it gives a number, NaN where it
+    gives NaN."""
+    import torch
+    n_codes = 16 if fmt == E2M1 else 256
+    K = 256                                        # 8 groups of 32 per row
+    vals = np.tile(np.arange(n_codes, dtype=np.uint8), K // n_codes)
+    codes_row = (vals[0::2] | (vals[1::2] << 4)).astype(np.uint8) if fmt == E2M1 else vals
+    codes = np.tile(codes_row[None, :], (256, 1))
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], K // 32, axis=1)
+    for dt, odt in ((torch.bfloat16, oracle.BF16), (torch.float32, oracle.F32)):
+        d = mx.mx_dequantize(fmt, torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), K, dtype=dt)
+        torch.cuda.synchronize()
+        want = oracle.dequantize(fmt, codes, scales, K, odt)
+        want_f = W.bf16_bits_to_f32(want) if odt == oracle.BF16 else want.view(np.float32)
+        nan = np.isnan(want_f)
+        assert nan[255].all() and nan.any(axis=1).sum() == (1 if fmt == E2M1 else 256)
+        assert np.array_equal(np.isnan(d.float().cpu().numpy()), nan), f"NaN positions {dt} fmt{fmt}"
+        assert_bits_equal(bits_of(d)[~nan], want[~nan], f"every code and scale {dt} fmt{fmt}")
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
 def test_exhaustive_reachable_pairs(mx, fmt):
     x = reachable_domain_matrix(fmt)
     check_qdq(mx, fmt, x, "exhaustive")
