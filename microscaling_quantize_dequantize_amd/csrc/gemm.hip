@@ -66,6 +66,19 @@ struct GemmShape {
   static constexpr int NG = BK / 32;                 // scale groups per slice
 };
 
+// Barrier that publishes LDS written by this workgroup's buffer loads with
+// an LDS destination: each wave first waits for all of its own vector-memory
+// operations (vmcnt(0)), so that after the barrier every wave's loads have
+// landed.  A plain __syncthreads() does not imply that wait at workgroup
+// scope: the compiler inserts it only where it sees a dependence, and across
+// the k-loop's back-edge it did not (one of the two barriers per iteration
+// went without it, so a slice could be read before other waves' loads of it
+// had landed).
+static __device__ __forceinline__ void publish_lds_loads() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+}
+
 static __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, RSRC_FLAGS);
 }
@@ -73,7 +86,8 @@ static __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p
 // Scale layouts: SL 0 row-major bytes; SL 1 blocked (a wave's words for its
 // 8 tiles and one 256-deep k-span are two 1 KB loads straight into LDS);
 // SL 2 row-major with groups % NG == 0, so a row's NG bytes of a slice are
-// one aligned load.
+// whole aligned dwords, also loaded straight into LDS with the codes (the
+// group-parity split is done when the words are read).
 template <int FMT, int OUT, int SL, bool TAIL>
 __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                                                  const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
@@ -84,9 +98,15 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   constexpr int CBSZ = FMT == 0 ? 4 : 0;  // FP4 E2M1 : FP8 E4M3
   constexpr int NWB = SL == 1 ? 4 * (TI + TJ) * 64 : 4;   // blocked words per slot
   constexpr int NWR = SL == 1 ? 4 : 2 * (BM + BN);        // row-major words per slot
+  // row-major scales straight into LDS (E4M3, SL 2: one dword per row and
+  // slice) or through registers (SL 0, and E2M1 SL 2, whose two dwords per
+  // row would take twice the LDS-destination loads of one 8-byte load per
+  // thread: measured 6% slower, while E4M3 gained 9%)
+  constexpr bool SDMA = SL == 2 && FMT == 1;
+  constexpr bool SREG = SL == 0 || (SL == 2 && FMT == 0);
   __shared__ __attribute__((aligned(1024))) uint8_t sm0[SLOT], sm1[SLOT];
   __shared__ __attribute__((aligned(1024))) unsigned wb0[NWB], wb1[NWB];
-  __shared__ __attribute__((aligned(16))) unsigned wr0[NWR], wr1[NWR];
+  __shared__ __attribute__((aligned(1024))) unsigned wr0[NWR], wr1[NWR];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -153,13 +173,22 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, MX_LDS(wb + wave * (TI + TJ) * 64), 16, va, span * 256, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, MX_LDS(wb + (wave * (TI + TJ) + TI) * 64), 16, vb, span * 256,
                                                0, 0);
+    } else if constexpr (SDMA) {
+      // the slice's NG = 4 scale bytes of every row, straight into LDS as
+      // [row][4]: wave w takes rows 64w..64w+63 of each operand, a dword per
+      // lane
+      static_assert(NG == 4, "one dword per row");
+      unsigned *wr = decltype(Pc)::value ? wr1 : wr0;
+      const unsigned voff = (unsigned)((64 * wave + lane) * groups);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, MX_LDS(wr + 64 * wave), 4, voff, kq * NG, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, MX_LDS(wr + BM + 64 * wave), 4, voff, kq * NG, 0, 0);
     }
   };
 
-  // ---- row-major scales (SL 0, 2): a thread loads its A row's and B row's
-  // NG bytes of a slice and stores them split by group parity: word h holds
-  // groups h, 2+h, 4+h, 6+h, so byte t is the scale of k-step t for lanes of
-  // half h ------------------------------------------------------------------
+  // ---- row-major scales through registers (SREG): a thread loads its A
+  // row's and B row's NG bytes of a slice and stores them split by group
+  // parity: word h holds groups h, 2+h, 4+h, 6+h, so byte t is the scale of
+  // k-step t for lanes of half h ----------------------------------------------
   struct RowScales {
     u32x2 a, b;
   };
@@ -167,14 +196,10 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
     const int kq = ks < nslices ? ks : nslices - 1;
     RowScales v{};
     if constexpr (SL == 2) {
-      if constexpr (NG == 8) {
-        v.a = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rAs, tid * groups, kq * NG, 0));
-        v.b = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rBs, tid * groups, kq * NG, 0));
-      } else {
-        v.a.x = __builtin_amdgcn_raw_buffer_load_b32(rAs, tid * groups, kq * NG, 0);
-        v.b.x = __builtin_amdgcn_raw_buffer_load_b32(rBs, tid * groups, kq * NG, 0);
-      }
-    } else if constexpr (SL == 0) {
+      // E2M1 (NG = 8): one aligned 8-byte load per row
+      v.a = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rAs, tid * groups, kq * NG, 0));
+      v.b = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rBs, tid * groups, kq * NG, 0));
+    } else {
       // bytes; groups past K re-read the row's last group, whose codes there
       // are zero
 #pragma unroll
@@ -222,14 +247,26 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
   };
-  auto read_word = [&](auto Pc, int f) -> unsigned {
+  // A scale word as read from LDS (SDMA: the row's 4 bytes, split by group
+  // parity only when the slice starts, so that the split does not wait for
+  // the read in the middle of the MFMAs it overlaps), and its value: byte t
+  // is the scale of k-step t for lanes of half h.
+  using Word = typename std::conditional<SDMA, u32x2, unsigned>::type;
+  auto read_word = [&](auto Pc, int f) -> Word {
     if constexpr (SL == 1) {
       const unsigned *wb = decltype(Pc)::value ? wb1 : wb0;
       return wb[(wave * (TI + TJ) + f) * 64 + lane];
+    } else if constexpr (SDMA) {
+      const unsigned *wr = decltype(Pc)::value ? wr1 : wr0;
+      return u32x2{wr[f < TI ? wm + 32 * f + r : BM + wn + 32 * (f - TI) + r], 0u};
     } else {
       const unsigned *wr = decltype(Pc)::value ? wr1 : wr0;
       return wr[2 * (f < TI ? wm + 32 * f + r : BM + wn + 32 * (f - TI) + r) + h];
     }
+  };
+  auto word_value = [&](const Word &w) -> unsigned {
+    if constexpr (SDMA) return __builtin_amdgcn_perm(w.y, w.x, h ? 0x07050301u : 0x06040200u);  // groups h, 2+h
+    else return w;
   };
 
   f32x16 acc[TI][TJ];
@@ -265,17 +302,17 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
 
   // fragments of the next k-step to run, and the scale words of its slice
   Frag fr[2][TI + TJ];
-  unsigned wd[TI + TJ];
-  RowScales rs_next{};  // row-major scales of the slice after next (SL 0, 2)
+  Word wd[TI + TJ];
+  RowScales rs_next{};  // row-major scales of the slice after next (SREG)
 
   if (nslices > 0) {
     load_slice(P0{}, 0);
     load_slice(P1{}, 1);
-    if constexpr (SL != 1) {
+    if constexpr (SREG) {
       store_row_scales(P0{}, load_row_scales(0));
       rs_next = load_row_scales(1);
     }
-    __syncthreads();
+    publish_lds_loads();
 #pragma unroll
     for (int f = 0; f < TI + TJ; ++f) {
       fr[0][f] = read_frag(P0{}, f, 0);
@@ -289,10 +326,15 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
     using Q = std::integral_constant<int, P ^ 1>;
     // scale byte of k-step t: blocked E4M3 slices are half a span
     auto byte_of = [](auto T) { return std::integral_constant<int, (SL == 1 && FMT == 1 ? 2 * P : 0) + decltype(T)::value>{}; };
+    // the slice's scale words (wd is refilled with the next slice's before
+    // the last k-step)
+    unsigned wcur[TI + TJ];
+#pragma unroll
+    for (int f = 0; f < TI + TJ; ++f) wcur[f] = word_value(wd[f]);
     // k-steps 0..NS-2, each reading the next step's fragments
     auto step = [&](auto T) {
       constexpr int t = decltype(T)::value;
-      mfma(byte_of(T), fr[t & 1], wd);
+      mfma(byte_of(T), fr[t & 1], wcur);
 #pragma unroll
       for (int f = 0; f < TI + TJ; ++f) fr[(t + 1) & 1][f] = read_frag(Pc, f, t + 1);
 #pragma unroll
@@ -306,19 +348,16 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       step(std::integral_constant<int, 1>{});
       step(std::integral_constant<int, 2>{});
     }
-    if constexpr (SL != 1) store_row_scales(Q{}, rs_next);
+    if constexpr (SREG) store_row_scales(Q{}, rs_next);
     // The last k-step: most of its MFMAs, then the barrier that publishes
     // the next slice (once every wave's loads have landed) and frees this
     // slice's slot, then the rest of the MFMAs overlapping the reads of the
     // next slice's first fragments and the loads of the slice after next
     // into this slot: those loads get a whole slice to land.
     constexpr int AFTER = 8;  // enough MFMA time to cover the reads
-    unsigned wcur[TI + TJ];
-#pragma unroll
-    for (int f = 0; f < TI + TJ; ++f) wcur[f] = wd[f];
     const auto last = byte_of(std::integral_constant<int, NS - 1>{});
     mfma(last, fr[(NS - 1) & 1], wcur, 0, TI * TJ - AFTER);
-    __syncthreads();
+    publish_lds_loads();
     mfma(last, fr[(NS - 1) & 1], wcur, TI * TJ - AFTER, TI * TJ);
 #pragma unroll
     for (int f = 0; f < TI + TJ; ++f) {
@@ -326,7 +365,7 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       wd[f] = read_word(Q{}, f);
     }
     load_slice(Pc, ks + 2);
-    if constexpr (SL != 1) rs_next = load_row_scales(ks + 2);
+    if constexpr (SREG) rs_next = load_row_scales(ks + 2);
 #pragma unroll
     for (int k = 0; k < AFTER; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
