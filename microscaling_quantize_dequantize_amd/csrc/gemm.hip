@@ -86,8 +86,9 @@ static __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p
 // Scale layouts: SL 0 row-major bytes; SL 1 blocked (a wave's words for its
 // 8 tiles and one 256-deep k-span are two 1 KB loads straight into LDS);
 // SL 2 row-major with groups % NG == 0, so a row's NG bytes of a slice are
-// whole aligned dwords, also loaded straight into LDS with the codes (the
-// group-parity split is done when the words are read).
+// whole aligned dwords; SL 3 (E2M1) row-major with groups % 16 == 0 and
+// 16-byte aligned scales, loaded by 16-byte spans of two slices (the
+// group-parity split of the LDS-loaded forms is done when a slice starts).
 template <int FMT, int OUT, int SL, bool TAIL>
 __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                                                  const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
@@ -97,16 +98,26 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   constexpr int BK = S::BK, NS = S::NS, NG = S::NG;
   constexpr int CBSZ = FMT == 0 ? 4 : 0;  // FP4 E2M1 : FP8 E4M3
   constexpr int NWB = SL == 1 ? 4 * (TI + TJ) * 64 : 4;   // blocked words per slot
-  constexpr int NWR = SL == 1 ? 4 : 2 * (BM + BN);        // row-major words per slot
-  // row-major scales straight into LDS (E4M3, SL 2: one dword per row and
-  // slice) or through registers (SL 0, and E2M1 SL 2, whose two dwords per
-  // row would take twice the LDS-destination loads of one 8-byte load per
-  // thread: measured 6% slower, while E4M3 gained 9%)
+  constexpr int NWR = SL == 1 || SL == 3 ? 4 : 2 * (BM + BN);  // row-major words per slot
+  // Row-major scales:
+  //  - E2M1, SL 3 (SPAN): 16 bytes of every row (16 groups, two slices)
+  //    straight into LDS, loaded every other slice into one of two span
+  //    buffers;
+  //  - E4M3, SL 2 (SDMA): one dword per row and slice straight into LDS
+  //    (9% faster than through registers);
+  //  - otherwise (SREG) through registers: E2M1 at SL 2 (its two dwords per
+  //    row and slice would take twice the LDS-destination loads of one
+  //    8-byte load per thread, measured 6% slower) and the byte loads of
+  //    SL 0.
+  static_assert(SL != 3 || FMT == 0, "spans are for E2M1");
+  constexpr bool SPAN = SL == 3;
   constexpr bool SDMA = SL == 2 && FMT == 1;
   constexpr bool SREG = SL == 0 || (SL == 2 && FMT == 0);
+  constexpr int NSP = SPAN ? (BM + BN) * 16 : 16;       // span buffer bytes
   __shared__ __attribute__((aligned(1024))) uint8_t sm0[SLOT], sm1[SLOT];
   __shared__ __attribute__((aligned(1024))) unsigned wb0[NWB], wb1[NWB];
   __shared__ __attribute__((aligned(1024))) unsigned wr0[NWR], wr1[NWR];
+  __shared__ __attribute__((aligned(1024))) uint8_t wsp[2][NSP];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -185,6 +196,20 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
     }
   };
 
+  // ---- row-major E2M1 scales by 16-byte spans (SPAN): span j holds groups
+  // 16j..16j+15 of every row, i.e. slices 2j and 2j+1, in buffer j % 2 as
+  // [row][16]; wave w loads rows 64w..64w+63 of each operand, a row per
+  // lane.  The launch takes this path only when the groups of a row are a
+  // multiple of 16, so no span reaches past its row -------------------------
+  auto load_span = [&](int j) {
+    const int nspans = nslices / 2;
+    const int jq = j < nspans ? j : nspans - 1;  // past the end: re-read the last span, unused
+    uint8_t *d = wsp[j & 1];
+    const unsigned voff = (unsigned)((64 * wave + lane) * groups + 16 * jq);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, MX_LDS(d + 64 * wave * 16), 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, MX_LDS(d + (BM + 64 * wave) * 16), 16, voff, 0, 0, 0);
+  };
+
   // ---- row-major scales through registers (SREG): a thread loads its A
   // row's and B row's NG bytes of a slice and stores them split by group
   // parity: word h holds groups h, 2+h, 4+h, 6+h, so byte t is the scale of
@@ -251,9 +276,14 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   // parity only when the slice starts, so that the split does not wait for
   // the read in the middle of the MFMAs it overlaps), and its value: byte t
   // is the scale of k-step t for lanes of half h.
-  using Word = typename std::conditional<SDMA, u32x2, unsigned>::type;
-  auto read_word = [&](auto Pc, int f) -> Word {
-    if constexpr (SL == 1) {
+  using Word = typename std::conditional<SDMA || SPAN, u32x2, unsigned>::type;
+  auto read_word = [&](auto Pc, int f, int ks) -> Word {
+    if constexpr (SPAN) {
+      // slice ks = 2j + P: bytes 8P..8P+7 of the row in span buffer j % 2
+      const uint8_t *b = wsp[(ks >> 1) & 1];
+      return *(const u32x2 *)(b + 16 * (f < TI ? wm + 32 * f + r : BM + wn + 32 * (f - TI) + r) +
+                              8 * decltype(Pc)::value);
+    } else if constexpr (SL == 1) {
       const unsigned *wb = decltype(Pc)::value ? wb1 : wb0;
       return wb[(wave * (TI + TJ) + f) * 64 + lane];
     } else if constexpr (SDMA) {
@@ -265,7 +295,7 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
     }
   };
   auto word_value = [&](const Word &w) -> unsigned {
-    if constexpr (SDMA) return __builtin_amdgcn_perm(w.y, w.x, h ? 0x07050301u : 0x06040200u);  // groups h, 2+h
+    if constexpr (SDMA || SPAN) return __builtin_amdgcn_perm(w.y, w.x, h ? 0x07050301u : 0x06040200u);  // groups h, 2+h, ..
     else return w;
   };
 
@@ -308,6 +338,10 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   if (nslices > 0) {
     load_slice(P0{}, 0);
     load_slice(P1{}, 1);
+    if constexpr (SPAN) {
+      load_span(0);
+      load_span(1);
+    }
     if constexpr (SREG) {
       store_row_scales(P0{}, load_row_scales(0));
       rs_next = load_row_scales(1);
@@ -316,7 +350,7 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
 #pragma unroll
     for (int f = 0; f < TI + TJ; ++f) {
       fr[0][f] = read_frag(P0{}, f, 0);
-      wd[f] = read_word(P0{}, f);
+      wd[f] = read_word(P0{}, f, 0);
     }
   }
 
@@ -362,9 +396,12 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
 #pragma unroll
     for (int f = 0; f < TI + TJ; ++f) {
       fr[0][f] = read_frag(Q{}, f, 0);
-      wd[f] = read_word(Q{}, f);
+      wd[f] = read_word(Q{}, f, ks + 1);
     }
     load_slice(Pc, ks + 2);
+    // SPAN: once slice 2j+1 is published, span j+2 goes into the buffer of
+    // span j, whose last words (slice 2j+1's) every wave has read
+    if constexpr (SPAN && P == 1) load_span((ks + 1) / 2 + 1);
     if constexpr (SREG) rs_next = load_row_scales(ks + 2);
 #pragma unroll
     for (int k = 0; k < AFTER; ++k) {
@@ -428,10 +465,14 @@ hipError_t launch_gemm(int fmt, const uint8_t *a, const uint8_t *as, const uint8
   if (scale_layout == 1) {
     run_gemm_k<1>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
   } else {
-    // one aligned load per row and slice when every slice's groups line up
+    // aligned loads per row when every slice's groups line up, 16-byte spans
+    // when the groups of a row are a multiple of 16 (E2M1)
     const int ng = fmt == 0 ? GemmShape<0>::NG : GemmShape<1>::NG;
     const bool aligned = (K / 32) % ng == 0 && (uintptr_t)as % 4 == 0 && (uintptr_t)bs % 4 == 0;
-    if (aligned) run_gemm_k<2>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
+    const bool spans = fmt == 0 && (K / 32) % 16 == 0 && (uintptr_t)as % 16 == 0 && (uintptr_t)bs % 16 == 0;
+    if (spans && out_dtype == 0) k_mx_gemm<0, 0, 3, false><<<grid, GT, 0, st>>>(a, as, b, bs, M, N, K, alpha, c);
+    else if (spans) k_mx_gemm<0, 1, 3, false><<<grid, GT, 0, st>>>(a, as, b, bs, M, N, K, alpha, c);
+    else if (aligned) run_gemm_k<2>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
     else run_gemm_k<0>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
   }
   return hipGetLastError();

@@ -133,6 +133,39 @@ def test_quantized_operands_within_bound(mx, fmt, shape):
         check_within_bound(got, ref, mb, alpha, dtype == torch.bfloat16)
 
 
+def offset_copy(t, off):
+    """t's bytes at byte offset `off` of a fresh 256-byte aligned buffer."""
+    import torch
+    buf = torch.zeros(t.numel() + 64, dtype=torch.uint8, device=t.device)
+    v = buf[off:off + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+@pytest.mark.parametrize("shape", [(300, 290, 1024), (64, 96, 3072)], ids=lambda s: "x".join(map(str, s)))
+def test_row_major_scale_paths_agree(mx, fmt, shape):
+    """The kernel loads row-major scales by 16-byte spans (E2M1, scales
+    16-byte aligned, groups per row a multiple of 16), by aligned dwords
+    (4-byte aligned) or by bytes (any alignment): the same scales at those
+    three alignments give the same bits, which also match the oracle's
+    bound."""
+    import torch
+    M, N, K = shape
+    ac, as_ = quantized_operand(fmt, M, K, 300 + fmt, 4)
+    bc, bs = quantized_operand(fmt, N, K, 400 + fmt, 4)
+    A, B = gpu_u8(ac), gpu_u8(bc)
+    outs = []
+    for off in (0, 4, 1):
+        sa, sb = offset_copy(gpu_u8(as_), off), offset_copy(gpu_u8(bs), off)
+        outs.append(mx.mx_matmul(fmt, A, sa, B, sb, K, dtype=torch.float32))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    ref = oracle.matmul(fmt, ac, as_, bc, bs, K)
+    mb = gemm_error_bound(fmt, oracle.dequantize_f64(fmt, ac, as_, K), oracle.dequantize_f64(fmt, bc, bs, K))
+    check_within_bound(values(outs[0]), ref, mb, 1.0, False)
+
+
 @pytest.mark.parametrize("fmt", [E2M1, E4M3])
 def test_quantize_then_matmul_chain(mx, fmt):
     """The pages' chain: quantize activations and weights on the GPU, then feed
