@@ -178,7 +178,12 @@ MX_API int mx_quantize_blocked(int fmt, const void *src, int64_t M, int64_t K,
  * QuTLASS support to vLLM", Purpose: MXFP4 matmul kernel with alpha and
  * bf16 output; review of the MXFP4 test: compared with a_dq @ b_dq^T).
  *   codes      16-byte aligned; c 16-byte aligned; row-major scales any
- *              alignment, blocked scales 4-byte aligned.
+ *              alignment, blocked scales 4-byte aligned.  Row-major
+ *              scales load fastest when K/32 is a multiple of 16 and
+ *              they are 16-byte aligned (MXFP4), next when K/32 is a
+ *              multiple of 8 (MXFP4) or 4 (MXFP8) and they are 4-byte
+ *              aligned; other shapes read them byte by byte (same
+ *              results, slower).
  *   K == 0 stores zeros.  M <= 65535 * 128; K <= 2^24 (MXFP4) or 2^23
  *   (MXFP8), else MX_ESHAPE.
  *   A scale byte of 0xFF (NaN) or an E4M3 NaN code gives NaN in the
