@@ -113,6 +113,12 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   constexpr bool SPAN = SL == 3;
   constexpr bool SDMA = SL == 2 && FMT == 1;
   constexpr bool SREG = SL == 0 || (SL == 2 && FMT == 0);
+  // E4M3 publishes each slice with two barriers (see the slice loop): its
+  // two k-steps per slice let the slot be refilled a quarter slice earlier
+  // (8% faster); E2M1's four k-steps gain an eighth, less than the second
+  // barrier costs (1% slower).
+  constexpr bool SPLIT = FMT == 1;
+  static_assert(DMA_W == 8, "16 code loads per wave and slice");
   constexpr int NSP = SPAN ? (BM + BN) * 16 : 16;       // span buffer bytes
   __shared__ __attribute__((aligned(1024))) uint8_t sm0[SLOT], sm1[SLOT];
   __shared__ __attribute__((aligned(1024))) unsigned wb0[NWB], wb1[NWB];
@@ -383,31 +389,65 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       step(std::integral_constant<int, 2>{});
     }
     if constexpr (SREG) store_row_scales(Q{}, rs_next);
-    // The last k-step: most of its MFMAs, then the barrier that publishes
-    // the next slice (once every wave's loads have landed) and frees this
-    // slice's slot, then the rest of the MFMAs overlapping the reads of the
-    // next slice's first fragments and the loads of the slice after next
-    // into this slot: those loads get a whole slice to land.
-    constexpr int AFTER = 8;  // enough MFMA time to cover the reads
+    constexpr int AFTER = 8;  // MFMAs after the barrier that publishes the next slice
     const auto last = byte_of(std::integral_constant<int, NS - 1>{});
-    mfma(last, fr[(NS - 1) & 1], wcur, 0, TI * TJ - AFTER);
-    publish_lds_loads();
-    mfma(last, fr[(NS - 1) & 1], wcur, TI * TJ - AFTER, TI * TJ);
+    if constexpr (!SPLIT) {
+      // The last k-step: most of its MFMAs, then the barrier that publishes
+      // the next slice (once every wave's loads have landed) and frees this
+      // slice's slot, then the rest of the MFMAs overlapping the reads of
+      // the next slice's first fragments and the loads of the slice after
+      // next into this slot: those loads get a whole slice to land.
+      mfma(last, fr[(NS - 1) & 1], wcur, 0, TI * TJ - AFTER);
+      publish_lds_loads();
+      mfma(last, fr[(NS - 1) & 1], wcur, TI * TJ - AFTER, TI * TJ);
 #pragma unroll
-    for (int f = 0; f < TI + TJ; ++f) {
-      fr[0][f] = read_frag(Q{}, f, 0);
-      wd[f] = read_word(Q{}, f, ks + 1);
-    }
-    load_slice(Pc, ks + 2);
-    // SPAN: once slice 2j+1 is published, span j+2 goes into the buffer of
-    // span j, whose last words (slice 2j+1's) every wave has read
-    if constexpr (SPAN && P == 1) load_span((ks + 1) / 2 + 1);
-    if constexpr (SREG) rs_next = load_row_scales(ks + 2);
+      for (int f = 0; f < TI + TJ; ++f) {
+        fr[0][f] = read_frag(Q{}, f, 0);
+        wd[f] = read_word(Q{}, f, ks + 1);
+      }
+      load_slice(Pc, ks + 2);
+      // SPAN: once slice 2j+1 is published, span j+2 goes into the buffer
+      // of span j, whose last words (slice 2j+1's) every wave has read
+      if constexpr (SPAN && P == 1) load_span((ks + 1) / 2 + 1);
+      if constexpr (SREG) rs_next = load_row_scales(ks + 2);
 #pragma unroll
-    for (int k = 0; k < AFTER; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TI + TJ) / AFTER * (FMT == 0 ? 1 : 2), 0);  // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x010, 3, 0);  // loads of the slice after next
+      for (int k = 0; k < AFTER; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TI + TJ) / AFTER * (FMT == 0 ? 1 : 2), 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x010, 3, 0);  // loads of the slice after next
+      }
+    } else {
+      // Two barriers.  A (LDS only): every wave has read this slice's last
+      // fragments (during the previous k-step), so the slot takes the loads
+      // of the slice after next before the last k-step starts.  B, before
+      // the last AFTER MFMAs, publishes the next slice: its loads were all
+      // issued before the (at least) 16 code loads just issued, and loads
+      // complete in order, so waiting until at most 16 are in flight
+      // suffices.  Both are written as asm, without the fences of
+      // __syncthreads(): at workgroup scope those wait for every
+      // outstanding load with an LDS destination (vmcnt(0)), which would
+      // give the new loads no time at all.
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if constexpr (SREG) rs_next = load_row_scales(ks + 2);  // before the loads: waiting for it must not wait for them
+      load_slice(Pc, ks + 2);
+      mfma(last, fr[(NS - 1) & 1], wcur, 0, TI * TJ - AFTER);
+#pragma unroll
+      for (int k = 0; k < TI * TJ - AFTER; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x010, 3, 0);  // loads of the slice after next
+      }
+      asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      mfma(last, fr[(NS - 1) & 1], wcur, TI * TJ - AFTER, TI * TJ);
+#pragma unroll
+      for (int f = 0; f < TI + TJ; ++f) {
+        fr[0][f] = read_frag(Q{}, f, 0);
+        wd[f] = read_word(Q{}, f, ks + 1);
+      }
+#pragma unroll
+      for (int k = 0; k < AFTER; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TI + TJ) / AFTER * (FMT == 0 ? 1 : 2), 0);  // LDS reads
+      }
     }
   };
 
