@@ -462,6 +462,44 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   // accumulator: lane l, register a holds C[8(a/4) + 4(l/32) + a%4][l%32]
+  //
+  // bf16 output of a tile inside C (N % 8 == 0): staged through LDS, so that
+  // C is written in 16-byte row pieces.  The accumulator layout holds
+  // columns, and its direct 2-byte stores cover 64-byte row segments (7% of
+  // the MXFP4 GEMM's time on 8192x8192x28672).  Each wave stages its 128 x
+  // 128 quarter in 32 KB of a slot: lane pairs exchange one value so that
+  // each lane writes bf16 pairs, then each lane reads 16-byte row pieces
+  // back and stores them.
+  if (OUT == 0 && m0 + BM <= M && n0 + BN <= N && N % 8 == 0) {
+    publish_lds_loads();  // every wave's loads have landed and its fragment reads are done
+    uint8_t *reg = (wave >> 1 ? sm1 : sm0) + (wave & 1) * TILE;  // a slot holds two 32 KB regions
+    const bool even = (r & 1) == 0;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int a = 0; a < 16; a += 2) {
+          const float x0 = alpha * acc[i][j][a], x1 = alpha * acc[i][j][a + 1];
+          const unsigned v0 = x0 != x0 ? 0x7FC0u : bf16_rne(x0), v1 = x1 != x1 ? 0x7FC0u : bf16_rne(x1);
+          // even lanes keep row a (columns r, r+1), odd lanes row a+1
+          // (columns r-1, r)
+          const unsigned q = dpp<DPP_QUAD_1032>(even ? v1 : v0);
+          const int row = 32 * i + 8 * (a / 4) + 4 * h + a % 4 + (even ? 0 : 1);
+          const int col = 32 * j + r - (even ? 0 : 1);
+          *(unsigned *)(reg + row * 256 + col * 2) = even ? (v0 | (q << 16)) : (q | (v1 << 16));
+        }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    uint16_t *c0 = (uint16_t *)C + (m0 + wm) * N + n0 + wn;
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      const int idx = 64 * k + lane, row = idx >> 4, piece = idx & 15;
+      const u32x4 v = *(const u32x4 *)(reg + row * 256 + piece * 16);
+      __builtin_nontemporal_store(v, (u32x4 *)(c0 + (int64_t)row * N + piece * 8));
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
