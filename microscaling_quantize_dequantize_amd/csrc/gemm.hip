@@ -278,10 +278,11 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
   };
-  // A scale word as read from LDS (SDMA: the row's 4 bytes, split by group
-  // parity only when the slice starts, so that the split does not wait for
-  // the read in the middle of the MFMAs it overlaps), and its value: byte t
-  // is the scale of k-step t for lanes of half h.
+  // A scale word as read from LDS (SDMA and SPAN: the row's NG bytes of the
+  // slice as loaded, split by group parity only when the slice starts, so
+  // that the split does not wait for the read in the middle of the MFMAs it
+  // overlaps), and its value: byte t is the scale of k-step t for lanes of
+  // half h.
   using Word = typename std::conditional<SDMA || SPAN, u32x2, unsigned>::type;
   auto read_word = [&](auto Pc, int f, int ks) -> Word {
     if constexpr (SPAN) {
