@@ -506,78 +506,46 @@ __device__ __forceinline__ u32x2 run_bf16(unsigned c, float sc) {
                __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, sc, true))};
 }
 
-// T16_THREADS per workgroup, T16_PER_CU resident per CU (LDS: 32 KiB of A
-// fragments plus a 4 KiB tile per wave), so T16_WAVES_PER_SIMD waves share
-// each SIMD: the register budget the compiler schedules for.
-constexpr int T16_THREADS = 256, T16_PER_CU = 3, T16_WAVES_PER_SIMD = 3;
+// T16_THREADS per workgroup; three fit a CU's LDS (32 KiB of A fragments
+// plus a 4 KiB tile per wave each), so T16_WAVES_PER_SIMD waves share each
+// SIMD: the register budget the compiler schedules for.  Each wave takes
+// T16_TPW consecutive tiles and keeps T16_NR of them in registers ahead of
+// the one it works on.
+constexpr int T16_THREADS = 256, T16_WAVES_PER_SIMD = 3, T16_TPW = 8, T16_NR = 4;
 
-// MX QDQ (bf16 in and out) with rotation 128 on 16-block tiles.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// MX QDQ (bf16 in and out) with rotation 128 on 16-block tiles.  A short-
+// lived workgroup: R (row-major 128 x 128 bf16) is copied into LDS, the A
+// fragments are formed from it with transposed reads (ds_read_b64_tr_b16:
+// within each 16-lane group, lane i receives element i%4 of the 8 bytes
+// that lanes 4r + i/4 address, r = 0..3, so when lane j addresses row
+// t0 + j/4 at column j0 + 4(j%4), lane i receives column j0 + i of rows
+// t0 .. t0+3), and the waves then stream their tiles.  The grid covers the
+// tensor once (up to a cap beyond which workgroups loop), so the hardware
+// dispatcher balances the work across CUs.
 template <int FMT>
 __global__ __launch_bounds__(T16_THREADS) __attribute__((amdgpu_waves_per_eu(T16_WAVES_PER_SIMD)))
-void k_rot128_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__ rot, int r,
+void k_rot128_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__ rot,
                   uint16_t *__restrict__ dst, int64_t n_blk) {
   static_assert(FMT == 0 || FMT == 1, "MX formats");
-  constexpr int THREADS = T16_THREADS;
+  constexpr int THREADS = T16_THREADS, TPW = T16_TPW, NR = T16_NR;
   constexpr int RB = 128, NJT = 8, NKB = 4, TB = 16;  // 16-wide j tiles, 32-deep k steps, blocks per tile
   constexpr int TP = TB * 16;                       // 16-byte input pieces per tile
   constexpr int NL = TP / 64;                       // coalesced pieces per lane
   constexpr int WAVES = THREADS / 64;
+  constexpr int RP = RB * RB / 8 / THREADS;         // 16-byte pieces of R per thread
+  static_assert(NKB == WAVES && NJT == 2 * WAVES && RP * THREADS * 8 == RB * RB && NR <= TPW,
+                "each wave forms the fragments of one k step");
   __shared__ u32x4 sA[NJT * NKB * 64];
   __shared__ u32x4 sT[WAVES][TP];
+  static_assert(sizeof(sA) == RB * RB * 2, "R is staged in the fragment buffer");
 
-  // R is staged in the A-fragment buffer itself (RB*RB*2 bytes = its size),
-  // then the fragments are built in the tile buffers and copied back.
-  static_assert(sizeof(sA) == RB * RB * 2 && sizeof(sT) >= 0, "R staging");
-  {
-    constexpr int RP = (RB * RB / 8 + THREADS - 1) / THREADS;
-    const int pieces = r * r / 8;
-    u32x4 rv[RP];
-#pragma unroll
-    for (int k = 0; k < RP; ++k) {
-      const int i = threadIdx.x + k * THREADS;
-      if (i < pieces) rv[k] = ((const u32x4 *)rot)[i];
-    }
-#pragma unroll
-    for (int k = 0; k < RP; ++k) {
-      const int i = threadIdx.x + k * THREADS;
-      if (i < pieces) sA[i] = rv[k];
-    }
-  }
-  __syncthreads();
-  // A fragment (jt, kb) of lane ln: Reff[32kb + 8(ln/16) + i][16jt + ln%16],
-  // gathered from R in sA into registers, then written over sA after a
-  // barrier
-  constexpr int FPT = (NJT * NKB * 64 + THREADS - 1) / THREADS;  // fragments per thread
-  u32x4 fa[FPT];
-  {
-    const uint16_t *Rs = (const uint16_t *)sA;
-#pragma unroll
-    for (int k = 0; k < FPT; ++k) {
-      const int idx = threadIdx.x + k * THREADS;
-      if (idx < NJT * NKB * 64) {
-        const int ln = idx & 63, f = idx >> 6, jt = f / NKB, kb = f % NKB;
-        const int j = jt * 16 + (ln & 15), t0 = 32 * kb + 8 * (ln >> 4);
-        unsigned w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          w[i] = (unsigned)reff(Rs, r, t0 + 2 * i, j) | ((unsigned)reff(Rs, r, t0 + 2 * i + 1, j) << 16);
-        fa[k] = u32x4{w[0], w[1], w[2], w[3]};
-      }
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < FPT; ++k) {
-    const int idx = threadIdx.x + k * THREADS;
-    if (idx < NJT * NKB * 64) sA[idx] = fa[k];
-  }
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63, p = lane >> 4, n = lane & 15;
-  u32x4 *T = sT[threadIdx.x >> 6];
+  const int lane = threadIdx.x & 63, p = lane >> 4, n = lane & 15, wave = threadIdx.x >> 6;
   const int64_t n_elem = n_blk * RB;
   const int64_t n_tiles = (n_blk + TB - 1) / TB;
-  const int64_t stride = (int64_t)gridDim.x * WAVES;
+  const int64_t n_units = (n_tiles + WAVES * TPW - 1) / (WAVES * TPW);
 
   // coalesced loads of one tile: lane piece 64q + lane (block (64q+lane)/16)
   auto load_tile = [&](int64_t tile, u32x4 *v) {
@@ -594,57 +562,103 @@ void k_rot128_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__
     }
   };
 
-  int64_t tile = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
-  u32x4 v[NL];
-  if (tile < n_tiles) load_tile(tile, v);
-  for (; tile < n_tiles; tile += stride) {
-    const int64_t e_tile = tile * TB * RB;
-    const bool full = e_tile + (int64_t)TP * 8 <= n_elem;
-    // 1. the tile into LDS (piece P = 64q + lane is block P/16, piece P%16)
+  // R and the first NR tiles of this wave, all loads in flight at once
+  int64_t unit = blockIdx.x;
+  u32x4 v[NR][NL];
+  {
+    u32x4 rv[RP];
 #pragma unroll
-    for (int q = 0; q < NL; ++q) T[slot16(4 * q + p, n)] = v[q];
-    wave_lds_sync();
-    // 2. B fragments: block n, pieces 4kb + p
-    u32x4 b[NKB];
+    for (int k = 0; k < RP; ++k) rv[k] = ((const u32x4 *)rot)[threadIdx.x + k * THREADS];
+    const int64_t t0 = (unit * WAVES + wave) * TPW;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) b[kb] = T[slot16(n, 4 * kb + p)];
-    wave_lds_sync();
-    // 3. rotate and QDQ, one 32-group (jt 2g, 2g+1) at a time
+    for (int t = 0; t < NR; ++t)
+      if (t0 + t < n_tiles) load_tile(t0 + t, v[t]);
 #pragma unroll
-    for (int gq = 0; gq < NJT / 2; ++gq) {
-      f32x4 acc[2] = {f32x4{}, f32x4{}};
+    for (int k = 0; k < RP; ++k) sA[threadIdx.x + k * THREADS] = rv[k];
+  }
+  __syncthreads();
+  {
+    // A fragment (jt, kb) of lane 16p + n: Reff[32kb + 8p + i][16jt + n],
+    // i = 0..7 (Reff = R at r = 128).  Wave w forms those of kb = w.
+    const uint16_t *Rs = (const uint16_t *)sA;
+    const int row = 32 * wave + 8 * p + (n >> 2), col = 4 * (n & 3);
+    u32x4 fa[NJT];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          acc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, sA[((2 * gq + hh) * NKB + kb) * 64 + lane]),
-              __builtin_bit_cast(bf16x8, b[kb]), acc[hh], 0, 0, 0);
-      unsigned sb, ca, cb;
-      float sc;
-      group16_codes<FMT>(acc[0], acc[1], sb, sc, ca, cb);
-      u32x2 oa = run_bf16<FMT>(ca, sc), ob = run_bf16<FMT>(cb, sc);
-      if (sb == 255u) oa = ob = u32x2{BF16_NAN | (BF16_NAN << 16), BF16_NAN | (BF16_NAN << 16)};
-      // run a: elements 32gq + 4p.. = piece 4gq + p/2, half p%2; run b: 2 pieces on
-      ((u32x2 *)T)[2 * slot16(n, 4 * gq + (p >> 1)) + (p & 1)] = oa;
-      ((u32x2 *)T)[2 * slot16(n, 4 * gq + 2 + (p >> 1)) + (p & 1)] = ob;
+    for (int jt = 0; jt < NJT; ++jt) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Rs + row * RB + 16 * jt + col));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Rs + (row + 4) * RB + 16 * jt + col));
+      const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+      fa[jt] = u32x4{a[0], a[1], b[0], b[1]};
     }
-    wave_lds_sync();
-    // 4. coalesced stores of the tile's outputs
-    u32x4 *gd = (u32x4 *)(dst + e_tile) + lane;
-    u32x4 o[NL];
+    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < NL; ++q) o[q] = T[slot16(4 * q + p, n)];
-    if (full) {
+    for (int jt = 0; jt < NJT; ++jt) sA[(jt * NKB + wave) * 64 + lane] = fa[jt];
+  }
+  __syncthreads();
+
+  u32x4 *T = sT[wave];
+  for (;;) {
+    const int64_t t0 = (unit * WAVES + wave) * TPW;
 #pragma unroll
-      for (int q = 0; q < NL; ++q) __builtin_nontemporal_store(o[q], gd + q * 64);
-    } else {
+    for (int t = 0; t < TPW; ++t) {
+      const int64_t tile = t0 + t;
+      if (tile >= n_tiles) break;
+      const int64_t e_tile = tile * TB * RB;
+      const bool full = e_tile + (int64_t)TP * 8 <= n_elem;
+      // 1. the tile into LDS (piece P = 64q + lane is block P/16, piece P%16)
 #pragma unroll
-      for (int q = 0; q < NL; ++q)
-        if (e_tile + (int64_t)(q * 64 + lane) * 8 < n_elem) __builtin_nontemporal_store(o[q], gd + q * 64);
+      for (int q = 0; q < NL; ++q) T[slot16(4 * q + p, n)] = v[t % NR][q];
+      wave_lds_sync();
+      // 2. B fragments: block n, pieces 4kb + p
+      u32x4 b[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) b[kb] = T[slot16(n, 4 * kb + p)];
+      wave_lds_sync();
+      // 3. rotate and QDQ, one 32-group (jt 2g, 2g+1) at a time
+#pragma unroll
+      for (int gq = 0; gq < NJT / 2; ++gq) {
+        f32x4 acc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            acc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, sA[((2 * gq + hh) * NKB + kb) * 64 + lane]),
+                __builtin_bit_cast(bf16x8, b[kb]), acc[hh], 0, 0, 0);
+        unsigned sb, ca, cb;
+        float sc;
+        group16_codes<FMT>(acc[0], acc[1], sb, sc, ca, cb);
+        u32x2 oa = run_bf16<FMT>(ca, sc), ob = run_bf16<FMT>(cb, sc);
+        if (sb == 255u) oa = ob = u32x2{BF16_NAN | (BF16_NAN << 16), BF16_NAN | (BF16_NAN << 16)};
+        // run a: elements 32gq + 4p.. = piece 4gq + p/2, half p%2; run b: 2 pieces on
+        ((u32x2 *)T)[2 * slot16(n, 4 * gq + (p >> 1)) + (p & 1)] = oa;
+        ((u32x2 *)T)[2 * slot16(n, 4 * gq + 2 + (p >> 1)) + (p & 1)] = ob;
+      }
+      wave_lds_sync();
+      // 4. coalesced stores of the tile's outputs
+      u32x4 *gd = (u32x4 *)(dst + e_tile) + lane;
+      u32x4 o[NL];
+#pragma unroll
+      for (int q = 0; q < NL; ++q) o[q] = T[slot16(4 * q + p, n)];
+      if (full) {
+#pragma unroll
+        for (int q = 0; q < NL; ++q) __builtin_nontemporal_store(o[q], gd + q * 64);
+      } else {
+#pragma unroll
+        for (int q = 0; q < NL; ++q)
+          if (e_tile + (int64_t)(q * 64 + lane) * 8 < n_elem) __builtin_nontemporal_store(o[q], gd + q * 64);
+      }
+      wave_lds_sync();
+      // the tile NR ahead into the registers just freed (issued after this
+      // tile's stores, so waiting for it never waits for them)
+      if (t + NR < TPW && tile + NR < n_tiles) load_tile(tile + NR, v[t % NR]);
     }
-    wave_lds_sync();
-    if (tile + stride < n_tiles) load_tile(tile + stride, v);
+    unit += gridDim.x;
+    if (unit >= n_units) break;
+    const int64_t t1 = (unit * WAVES + wave) * TPW;
+#pragma unroll
+    for (int t = 0; t < NR; ++t)
+      if (t1 + t < n_tiles) load_tile(t1 + t, v[t]);
   }
 }
 
@@ -771,8 +785,8 @@ static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
   return (unsigned)(g < cap ? g : cap);
 }
 
-// MX QDQ at RB = 128 runs on 16-block tiles (k_rot128_t16), a persistent
-// grid of T16_PER_CU workgroups per CU.  Quantize (whose outputs are a
+// MX QDQ at RB = 128 runs on 16-block tiles (k_rot128_t16), one workgroup
+// per T16_TPW tiles of each of its waves.  Quantize (whose outputs are a
 // quarter of QDQ's) measured as fast or faster on 32-block tiles, and NVFP4
 // stays there too: its 16-groups span four lanes here instead of two, so
 // each lane repeats the group's scale steps for twice as many elements
@@ -783,9 +797,10 @@ static void run_staged(const void *src, const void *rot, int r, void *dst, uint8
                        int64_t n, hipStream_t st, const BlockedScales *bl, const float *gp = nullptr) {
   const int64_t n_blk = n / RB;
   if constexpr (RB == 128 && FMT != 2 && OP == OP_QDQ) {
-    const unsigned g = persistent_grid((n_blk + 15) / 16, T16_THREADS / 64, T16_PER_CU);
-    k_rot128_t16<FMT><<<g, T16_THREADS, 0, st>>>((const uint16_t *)src, (const uint16_t *)rot, r,
-                                                 (uint16_t *)dst, n_blk);
+    const int64_t units = ((n_blk + 15) / 16 + (T16_THREADS / 64) * T16_TPW - 1) / ((T16_THREADS / 64) * T16_TPW);
+    const unsigned g = (unsigned)(units < ((int64_t)1 << 30) ? units : ((int64_t)1 << 30));
+    k_rot128_t16<FMT><<<g, T16_THREADS, 0, st>>>((const uint16_t *)src, (const uint16_t *)rot, (uint16_t *)dst,
+                                                 n_blk);
     return;
   } else {
     using Cfg = StagedCfg<RB>;
