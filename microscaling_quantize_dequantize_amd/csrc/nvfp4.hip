@@ -94,15 +94,31 @@ __global__ __launch_bounds__(NV_T) void k_nv_qdq(const u32x4 *__restrict__ src, 
 // Quantize with one lane per 16-group (two 16-byte pieces): the scale, its
 // value and the quotient g / value are computed once per group instead of
 // by both lanes of a pair, and the abs-max needs no lane exchange (measured
-// 11% faster on the 8192 x 57344 layer).  QDQ stays on lane pairs: here its
-// output would be two 16-byte stores 32 bytes apart per lane, which measured
-// 6% slower than the pairs' contiguous stores.
+// 11% faster on the 8192 x 57344 layer).  Each wave takes 64 consecutive
+// groups: its loads stay coalesced (lane l reads pieces l and 64 + l) and a
+// wave-private LDS buffer hands each lane its group's two pieces, 9% faster
+// than each lane loading its own 32 bytes.  QDQ stays on lane pairs: here
+// its output would be two 16-byte stores 32 bytes apart per lane, which
+// measured 6% slower than the pairs' contiguous stores.
 template <bool FAST>
 __device__ __forceinline__ void nv_quant_loop(const u32x4 *__restrict__ src, uint8_t *__restrict__ codes,
                                               uint8_t *__restrict__ scales, const NvTensor &t, int64_t n_groups) {
+  __shared__ u32x4 buf[NV_T / 64][128];
+  const int lane = threadIdx.x & 63;
+  u32x4 *B = buf[threadIdx.x >> 6];
   const int64_t stride = (int64_t)gridDim.x * NV_T;
-  for (int64_t q = (int64_t)blockIdx.x * NV_T + threadIdx.x; q < n_groups; q += stride) {
-    const u32x4 w0 = __builtin_nontemporal_load(src + 2 * q), w1 = __builtin_nontemporal_load(src + 2 * q + 1);
+  for (int64_t base = (int64_t)blockIdx.x * NV_T + (threadIdx.x & ~63); base < n_groups; base += stride) {
+    const int64_t p0 = 2 * base, np = 2 * n_groups;
+    const u32x4 lo = p0 + lane < np ? __builtin_nontemporal_load(src + p0 + lane) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 hi = p0 + 64 + lane < np ? __builtin_nontemporal_load(src + p0 + 64 + lane) : u32x4{0u, 0u, 0u, 0u};
+    B[lane] = lo;
+    B[64 + lane] = hi;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const u32x4 w0 = B[2 * lane], w1 = B[2 * lane + 1];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const int64_t q = base + lane;
     unsigned mb;
     {
       u16x2 a = __builtin_bit_cast(u16x2, w0.x & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2, w0.y & 0x7FFF7FFFu);
@@ -118,8 +134,10 @@ __device__ __forceinline__ void nv_quant_loop(const u32x4 *__restrict__ src, uin
     const float amax = __uint_as_float(mb << 16);
     const unsigned sb = nv_scale_byte(amax * t.c6);
     const float m = nv_mul<FAST>(t, nv_scale_value(sb));
-    __builtin_nontemporal_store(u32x2{nv_codes(w0, m), nv_codes(w1, m)}, (u32x2 *)codes + q);
-    scales[q] = (uint8_t)sb;
+    if (q < n_groups) {
+      __builtin_nontemporal_store(u32x2{nv_codes(w0, m), nv_codes(w1, m)}, (u32x2 *)codes + q);
+      scales[q] = (uint8_t)sb;
+    }
   }
 }
 
