@@ -827,10 +827,20 @@ static void run_direct(int dtype, const void *src, const void *rot, int r, void 
     k_rot_f32<FMT, OP, RB><<<g, DTHREADS, 0, st>>>((const float *)src, (const float *)rot, r, dst, n_blk);
 }
 
+// Block size of the staged (bf16) kernels: RB = max(r, 32), except that
+// r = 16 and r = 32 run as RB = 64 (four or two copies of R on the
+// diagonal) whenever the tensor is a whole number of 64-blocks and, for
+// blocked scales, a row holds a whole number of them: the RB = 64 kernel
+// streams its 4 KiB tiles faster than the RB = 32 kernel its 2 KiB ones.
+static int staged_rb(int r, int64_t n, const BlockedScales *bl) {
+  if (r <= 32 && n % 64 == 0 && (bl == nullptr || bl->groups % 2 == 0)) return 64;
+  return r < 32 ? 32 : r;
+}
+
 template <int FMT, int OP>
 static void dispatch_rb(int dtype, const void *src, const void *rot, int r, void *dst, uint8_t *codes,
                         uint8_t *scales, int64_t n, hipStream_t st, const BlockedScales *bl) {
-  const int rb = r < 32 ? 32 : r;
+  const int rb = dtype == 0 && OP != OP_ROTATE ? staged_rb(r, n, bl) : (r < 32 ? 32 : r);
   if (dtype == 0 && OP != OP_ROTATE) {
     if (rb == 32) run_staged<FMT, OP, 32>(src, rot, r, dst, codes, scales, n, st, bl);
     else if (rb == 64) run_staged<FMT, OP, 64>(src, rot, r, dst, codes, scales, n, st, bl);
@@ -844,7 +854,7 @@ static void dispatch_rb(int dtype, const void *src, const void *rot, int r, void
 
 hipError_t launch_nv_rot(int op, const void *src, const void *rot, int r, void *dst, uint8_t *codes,
                          uint8_t *scales, const float *gp, int64_t n, hipStream_t st) {
-  const int rb = r < 32 ? 32 : r;
+  const int rb = staged_rb(r, n, nullptr);
   if (op == OP_QDQ) {
     if (rb == 32) run_staged<2, OP_QDQ, 32>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
     else if (rb == 64) run_staged<2, OP_QDQ, 64>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);

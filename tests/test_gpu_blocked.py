@@ -67,8 +67,8 @@ def test_quantize_blocked_matches_oracle(mx, fmt, shape):
 
 
 @pytest.mark.parametrize("fmt", [E2M1, E4M3])
-@pytest.mark.parametrize("r,shape", [(16, (77, 224)), (32, (33, 288)), (64, (45, 384)), (128, (129, 1152))],
-                         ids=lambda v: str(v))
+@pytest.mark.parametrize("r,shape", [(16, (77, 224)), (16, (6, 96)), (32, (33, 288)), (32, (10, 160)), (64, (45, 384)),
+                                     (128, (129, 1152))], ids=lambda v: str(v))
 def test_quantize_blocked_rotated_equals_rowmajor(mx, fmt, r, shape):
     import torch
     M, K = shape

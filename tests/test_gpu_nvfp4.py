@@ -137,8 +137,8 @@ def test_unrotated_full_size(mx):
     assert_bits_equal(bits_of(qdq)[rows], oracle.nv_qdq(x[rows], g, threads=THREADS), "full-size qdq rows")
 
 
-@pytest.mark.parametrize("r,shape", [(16, (64, 256)), (32, (33, 288)), (64, (45, 384)), (128, (129, 1152))],
-                         ids=lambda v: str(v))
+@pytest.mark.parametrize("r,shape", [(16, (64, 256)), (16, (6, 96)), (32, (33, 288)), (32, (10, 160)), (64, (45, 384)),
+                                     (128, (129, 1152))], ids=lambda v: str(v))
 def test_rotated_within_band(mx, r, shape):
     import torch
     M, K = shape

@@ -152,6 +152,21 @@ def test_rot128_qdq_work_unit_edges(mx, fmt, shape):
     _qdq_band(mx, fmt, x, W.hadamard_rotation(128), 128)
 
 
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+@pytest.mark.parametrize("r,shape", [(16, (6, 96)), (16, (10, 160)), (32, (6, 96)), (32, (10, 160)), (16, (5, 96))],
+                         ids=lambda v: str(v))
+def test_small_rotations_across_rows(mx, fmt, r, shape):
+    """Rotations of 16 and 32 run on 64-element blocks (two or four copies of
+    R on the diagonal) when the tensor is a whole number of them, so with K
+    not a multiple of 64 a block holds the end of one row and the start of
+    the next: QDQ and quantize stay within the oracle's band.  (5, 96) is not
+    a whole number of 64-blocks and takes the 32-element blocks."""
+    x = W.random_bf16(shape, seed=shape[0] * 13 + r + fmt)
+    R = W.hadamard_rotation(r)
+    _qdq_band(mx, fmt, x, R, r)
+    _quant_band(mx, fmt, x, R, r)
+
+
 def test_c3_mxfp4_qdq_rot32(mx):
     x = W.generate("c3")
     stats = _qdq_band(mx, E2M1, x, W.hadamard_rotation(32), 32)
