@@ -7,9 +7,9 @@
 //
 // Since K is a multiple of r and of 32, chunks never straddle rows and the
 // matrix is one flat array of r-chunks.  The kernels work on blocks of
-// RB = max(r, 32) elements with the block-diagonal matrix diag(R, ..., R) of
-// size RB (r = 16 gives diag(R, R)), so that every 32-group lies inside one
-// block.
+// RB >= max(r, 32) elements with the block-diagonal matrix diag(R, ..., R)
+// of size RB, so that every 32-group lies inside one block (RB = max(r, 32),
+// or 64 for r = 16 and 32 where the shape allows; see staged_rb).
 //
 // The contraction Y^T = Reff^T . X^T runs on v_mfma_f32_32x32x16_bf16 (bf16
 // products are exact in fp32; accumulation in fp32):
@@ -194,7 +194,7 @@ __device__ __forceinline__ void group_fp8_bytes(const unsigned c[4], unsigned sb
 // per-tensor multiplier *gp).
 // SL (OP_QUANT only): 0 = row-major scales, 1 = the blocked layout `bl`.
 // Launch shape of the 32-block staged kernels (k_rot_bf16): workgroup size,
-// workgroups per CU in the grid (per_cu) and workgroups resident on a CU at
+// workgroups per CU in the grid (per_cu; per_cu_qdq for QDQ) and workgroups resident on a CU at
 // once (resident).  LDS per workgroup is RB*RB*2 bytes of A fragments plus a
 // 64*RB-byte tile buffer per wave; the launch pads it so that no more than
 // `resident` fit in a CU's LDS, and the kernel's register budget lets that
@@ -203,13 +203,14 @@ __device__ __forceinline__ void group_fp8_bytes(const unsigned c[4], unsigned sb
 // QDQ and quantize): one resident workgroup (16 waves) for RB = 32 and two
 // (16 waves) for RB = 64 run 2-3% faster than the 32 and 24 waves that fit
 // otherwise.  For RB = 64 a grid of 32 per CU (about 3.5 tiles per wave) is
-// fastest; for RB = 128 (quantize and NVFP4) a persistent grid of exactly
-// the resident count (a grid that is not a multiple of it leaves a partial
-// last round).
+// fastest for quantize and 48 (about 2.3) for QDQ (per_cu_qdq; 1-2% faster
+// than 32 for QDQ, 3-4% slower for blocked-scale quantize); for RB = 128
+// (quantize and NVFP4) a persistent grid of exactly the resident count (a
+// grid that is not a multiple of it leaves a partial last round).
 template <int RB> struct StagedCfg;
-template <> struct StagedCfg<32> { static constexpr int threads = 1024, per_cu = 8, resident = 1; };
-template <> struct StagedCfg<64> { static constexpr int threads = 512, per_cu = 32, resident = 2; };
-template <> struct StagedCfg<128> { static constexpr int threads = 256, per_cu = 2, resident = 2; };
+template <> struct StagedCfg<32> { static constexpr int threads = 1024, per_cu = 8, per_cu_qdq = 8, resident = 1; };
+template <> struct StagedCfg<64> { static constexpr int threads = 512, per_cu = 32, per_cu_qdq = 48, resident = 2; };
+template <> struct StagedCfg<128> { static constexpr int threads = 256, per_cu = 2, per_cu_qdq = 2, resident = 2; };
 
 constexpr int LDS_PER_CU = 160 * 1024;
 
@@ -804,7 +805,7 @@ static void run_staged(const void *src, const void *rot, int r, void *dst, uint8
     return;
   } else {
     using Cfg = StagedCfg<RB>;
-    const unsigned g = persistent_grid((n_blk + 31) / 32, Cfg::threads / 64, Cfg::per_cu);
+    const unsigned g = persistent_grid((n_blk + 31) / 32, Cfg::threads / 64, OP == OP_QDQ ? Cfg::per_cu_qdq : Cfg::per_cu);
     if constexpr (OP == OP_QUANT && FMT != 2) {
       if (bl != nullptr) {
         k_rot_bf16<FMT, OP, RB, Cfg::threads, 1><<<g, Cfg::threads, staged_lds_pad<RB>(), st>>>(
