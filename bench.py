@@ -182,7 +182,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the MX QDQ path shards by rows with no exchange, "
-              "and this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+              "so one GPU's throughput is the measurement; use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
