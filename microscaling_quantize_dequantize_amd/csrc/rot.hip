@@ -34,7 +34,6 @@
 // of bank conflicts.
 #include "launch.h"
 #include "mx_device.h"
-#include <type_traits>
 
 namespace mx {
 
