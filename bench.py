@@ -13,9 +13,25 @@ bytes per element: QDQ 2 + 2; quantize 2 + 0.5 + 1/32 (MXFP4) or 2 + 1 + 1/32
 (MXFP8); the rotation matrix (<= 32 KiB) is not counted.
 
 Each launch is bracketed by HIP events on the stream it runs on (the binding
-launches on torch's current stream); the roofline entry uses the average
-launch duration of the kernel with the largest share of the step.  A plain
-device copy of the layer is timed the same way as a measured copy ceiling.
+launches on torch's current stream).  The roofline entry is the launch of
+the step with the longest average duration: its algorithmic bytes over that
+duration, against 8 TB/s.
+
+Beside the step:
+  - measured ceilings: a 16-byte streaming copy, read-only and write-only
+    kernel (bench_ceiling.hip, built outside the library; the best of three
+    launch shapes each) and the runtime's device-to-device copy, all on the
+    layer's bytes; every kernel also reports its fraction of the copy
+    ceiling;
+  - the other workloads, each timed on its own seeded input: MXFP4 QDQ of a
+    128 x 4096 activation (launch-bound, timed by graph replay), MXFP8 QDQ
+    and quantize of 8192 x 8192, MXFP4 QDQ with rotation 32 of 4096 x 8192,
+    MXFP4 quantize with rotation 128 and without of 8192 x 28672, and MXFP4
+    and MXFP8 QDQ with rotation none / 16 / 64 of the 8192 x 8192 and
+    28672 x 8192 layers; inputs under 1 GB are evicted from the 256 MB
+    last-level cache between timed launches by a 512 MiB write;
+  - dequantize, the layer read as 57344 x 8192, NVFP4, blocked scales and
+    the GEMM that consumes the quantized layer.
 The CPU baseline runs the oracle (unchanged) on a bounded row sample of the
 same layer and variants, on the host's cores.
 
@@ -169,6 +185,161 @@ def timed_graph(fn, reps):
 GEMM_PEAK_TFLOPS = {0: 10100.0, 1: 5000.0}  # MI355X dense fp4 / fp8 matrix peaks
 
 
+def ceiling_lib():
+    """The streaming ceiling kernels (bench_ceiling.so, built by
+    __graft_entry__.build())."""
+    import ctypes
+    path = os.path.join(ROOT, "bench_ceiling.so")
+    if not os.path.exists(path):
+        raise SystemExit("bench_ceiling.so is missing: run `python __graft_entry__.py build` first")
+    L = ctypes.CDLL(path)
+    vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint
+    L.ceil_copy.argtypes = [vp, vp, i64, i32, vp]
+    L.ceil_read.argtypes = [vp, i64, vp, u32, i32, vp]
+    L.ceil_write.argtypes = [vp, i64, u32, i32, vp]
+    for f in (L.ceil_copy, L.ceil_read, L.ceil_write):
+        f.restype = i32
+    return L
+
+
+def _stream_ptr():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def measure_ceilings(L, x, copy_dst):
+    """Best GB/s of the copy, read-only and write-only kernels over the
+    launch shapes (1, 2 or 4 pieces per thread), and of the runtime's
+    device-to-device copy, each on the bytes of x."""
+    import torch
+    nbytes = x.numel() * x.element_size()
+    sink = torch.zeros(64, dtype=torch.int32, device=x.device)
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"ceiling kernel returned {rc}")
+
+    kinds = {
+        "copy": (lambda u: check(L.ceil_copy(x.data_ptr(), copy_dst.data_ptr(), nbytes, u, _stream_ptr())),
+                 2 * nbytes),
+        "read": (lambda u: check(L.ceil_read(x.data_ptr(), nbytes, sink.data_ptr(), 0x9E3779B9, u, _stream_ptr())),
+                 nbytes),
+        "write": (lambda u: check(L.ceil_write(copy_dst.data_ptr(), nbytes, 0x3F803F80, u, _stream_ptr())),
+                  nbytes),
+    }
+    out = {}
+    for kind, (fn, b) in kinds.items():
+        best = None
+        for u in (1, 2, 4):
+            fn(u)
+            avg, mn = timed(lambda: fn(u), 10)
+            gbps = b / (avg * 1e-3) / 1e9
+            if best is None or gbps > best[0]:
+                best = (gbps, u, avg)
+        out[kind] = {"GBps": round(best[0], 1), "pieces_per_thread": best[1], "avg_us": round(best[2] * 1e3, 2),
+                     "bytes": int(b)}
+    for _ in range(2):
+        copy_dst.copy_(x)
+    avg, _ = timed(lambda: copy_dst.copy_(x), 10)
+    out["runtime_copy"] = {"GBps": round(2 * nbytes / (avg * 1e-3) / 1e9, 1), "avg_us": round(avg * 1e3, 2),
+                           "bytes": int(2 * nbytes)}
+    return out
+
+
+def timed_flushed(fn, reps, flush):
+    """As timed(), with flush() (a 512 MiB write that evicts the 256 MB
+    last-level cache) between launches, outside the events."""
+    import numpy as np
+    import torch
+    ms = []
+    for _ in range(reps):
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    return float(np.mean(ms)), float(np.min(ms))
+
+
+# The other workloads: (name, [(op, fmt, rotation), ...]).  The 8192 x 57344
+# layer is the step itself.
+CONFIGS = [
+    ("c1", [("qdq", 0, 0)]),
+    ("c2", [("qdq", 1, 0), ("quantize", 1, 0)]),
+    ("c3", [("qdq", 0, 32)]),
+    ("c4", [("quantize", 0, 128), ("quantize", 0, 0)]),
+    ("c5a", [("qdq", f, r) for f in (0, 1) for r in (0, 16, 64)]),
+    ("c5c", [("qdq", f, r) for f in (0, 1) for r in (0, 16, 64)]),
+]
+
+CONFIG_TEXT = {
+    "c1": "128x4096 activation, N(0,1) with 0.1% x50 outliers and 4 zero groups",
+    "c2": "8192x8192, 0.5 * Student-t(4), every 64th row x1000",
+    "c3": "4096x8192, N(0,1) with LogNormal(0,1) column scales",
+    "c4": "8192x28672 down-projection input, Student-t(3)",
+    "c5a": "8192x8192 layer, N(0,0.02^2) with subnormal-range and saturating groups",
+    "c5c": "28672x8192 layer, N(0,0.02^2) with subnormal-range and saturating groups",
+}
+
+
+def time_configs(mx, W, flush, copy_gbps):
+    """Each workload on its own seeded input: average and minimum launch
+    time, GB/s, fraction of 8 TB/s and of the copy ceiling, and the rotated
+    over unrotated ratios."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    rows, ratios = [], {}
+    for name, vs in CONFIGS:
+        xb = W.generate(name)
+        M, K = xb.shape
+        n = M * K
+        x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+        del xb
+        dst = torch.empty_like(x)
+        codes = {0: torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                 1: torch.empty((M, K), dtype=torch.uint8, device=dev)}
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        times = {}
+        for op, fmt, r in vs:
+            R = None
+            if r:
+                Rb = W.hadamard_rotation(r)
+                R = torch.from_numpy(Rb.view(np.int16)).view(torch.bfloat16).to(dev)
+            cv = codes[fmt]
+            if op == "qdq":
+                fn = (lambda fmt=fmt, R=R: mx.mx_qdq(fmt, x, rot=R, dst=dst))
+            else:
+                fn = (lambda fmt=fmt, R=R, cv=cv: mx.mx_quantize(fmt, x, rot=R, codes=cv, scales=scales))
+            b = n * bytes_per_element(op, fmt)
+            for _ in range(2):
+                fn()
+            if name == "c1":
+                avg, mn = timed_graph(fn, 200)
+                how = "graph replay of 200 back-to-back launches (L2-resident, launch-bound)"
+            else:
+                avg, mn = timed_flushed(fn, 10, flush) if 2 * b < 1e9 else timed(fn, 10)
+                how = "events per launch" + (", cache evicted between launches" if 2 * b < 1e9 else "")
+            gbps = b / (avg * 1e-3) / 1e9
+            key = name_of(op, fmt, r)
+            times[key] = avg
+            rows.append({"config": name, "workload": CONFIG_TEXT[name], "M": M, "K": K, "kernel": key,
+                         "bytes": int(b), "avg_us": round(avg * 1e3, 2), "min_us": round(mn * 1e3, 2),
+                         "GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4),
+                         "frac_of_copy": round(gbps / copy_gbps, 4), "elements_per_s": round(n / (avg * 1e-3), 1),
+                         "timing": how})
+        for key, t in times.items():
+            op, f, rot = key.split("_")
+            base = f"{op}_{f}_rot0"
+            if rot != "rot0" and base in times:
+                ratios[f"{name}_{op}_{rot}_over_rot0_{f}"] = round(t / times[base], 3)
+        del x, dst, codes, scales
+        torch.cuda.empty_cache()
+    return rows, ratios
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +361,7 @@ def main():
 
     from microscaling_quantize_dequantize_amd import binding as mx
     from microscaling_quantize_dequantize_amd import workloads as W
+    CL = ceiling_lib()
 
     dev = torch.device("cuda:0")
     x_bits = W.generate(WORKLOAD)
@@ -225,7 +397,6 @@ def main():
 
     for _ in range(args.warmup):
         step()
-        copy_dst.copy_(x)
     torch.cuda.synchronize()
 
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in var]
@@ -321,15 +492,12 @@ def main():
         del cq, sq, a, b_, sa, sb, ba, bb
     del gc
 
-    # measured copy ceiling: device-to-device copy of the same layer
-    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-    for a, b in cev:
-        a.record()
-        copy_dst.copy_(x)
-        b.record()
-    torch.cuda.synchronize()
-    copy_ms = float(np.mean([a.elapsed_time(b) for a, b in cev]))
-    copy_gbps = 2 * n * 2 / (copy_ms * 1e-3) / 1e9
+    # measured ceilings on the layer's bytes
+    ceilings = measure_ceilings(CL, x, copy_dst)
+    copy_gbps = ceilings["copy"]["GBps"]
+    for e in extras:
+        if "GBps" in e:
+            e["frac_of_copy"] = round(e["GBps"] / copy_gbps, 4)
 
     per = []
     step_bytes = 0.0
@@ -352,6 +520,19 @@ def main():
              for f in ("mxfp4", "mxfp8")}
     ratio.update({f"quantize_rot128_over_rot0_{f}": round(
         by[f"quantize_{f}_rot128"]["avg_us"] / by[f"quantize_{f}_rot0"]["avg_us"], 3) for f in ("mxfp4", "mxfp8")})
+
+    # the other workloads, on their own inputs (the step's buffers freed first)
+    del x, dst, codes, scales, copy_dst
+    torch.cuda.empty_cache()
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush():
+        if CL.ceil_write(flush_buf.data_ptr(), flush_buf.numel(), 0, 1, _stream_ptr()) != 0:
+            raise RuntimeError("flush write failed")
+
+    config_rows, config_ratios = time_configs(mx, W, flush, copy_gbps)
+    ratio.update(config_ratios)
+    del flush_buf
 
     out = {
         "metric": METRIC,
@@ -377,6 +558,8 @@ def main():
                      "traffic": load_traffic(dom["kernel"])},
         "variants": per,
         "ratios": ratio,
+        "ceilings": ceilings,
+        "configs": config_rows,
         "outside_step": extras,
     }
     if not args.no_cpu:

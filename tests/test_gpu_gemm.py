@@ -207,8 +207,11 @@ def test_empty_and_bad_arguments(mx):
     b = torch.zeros((4, 16), dtype=torch.uint8, device="cuda")
     bs = torch.full((4, 1), 127, dtype=torch.uint8, device="cuda")
     assert mx.mx_matmul(E2M1, e, s, b, bs, 32).shape == (0, 4)
+    b48 = torch.zeros((4, 24), dtype=torch.uint8, device="cuda")
     with pytest.raises(mx.MXError):
-        mx.mx_matmul(E2M1, b, bs, b, bs, 48)  # K not a multiple of 32
+        mx.mx_matmul(E2M1, b48, bs, b48, bs, 48)  # K not a multiple of 32
+    with pytest.raises(ValueError):
+        mx.mx_matmul(E2M1, b, bs, b, bs, 64)  # codes too short for K
     with pytest.raises(ValueError):
         mx.mx_matmul(E2M1, b, bs, b, bs, 32, c=torch.empty((4, 5), device="cuda"))
 
