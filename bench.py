@@ -75,7 +75,7 @@ def name_of(op, fmt, r):
     return f"{op}_{'mxfp4' if fmt == 0 else 'mxfp8'}_rot{r}"
 
 
-STEP_SOURCES = ("unrot.hip", "rot.hip", "mx_device.h")  # what the step's kernels are built from
+STEP_SOURCES = ("unrot.hip", "rot.hip", "rotl.hip", "mx_device.h")  # what the step's kernels are built from
 
 
 def source_hash():
@@ -284,6 +284,11 @@ CONFIG_TEXT = {
 }
 
 
+def progress(msg):
+    """A phase of the run, on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def time_configs(mx, W, flush, copy_gbps):
     """Each workload on its own seeded input: average and minimum launch
     time, GB/s, fraction of 8 TB/s and of the copy ceiling, and the rotated
@@ -293,6 +298,7 @@ def time_configs(mx, W, flush, copy_gbps):
     dev = torch.device("cuda:0")
     rows, ratios = [], {}
     for name, vs in CONFIGS:
+        progress(f"workload {name}")
         xb = W.generate(name)
         M, K = xb.shape
         n = M * K
@@ -364,6 +370,7 @@ def main():
     CL = ceiling_lib()
 
     dev = torch.device("cuda:0")
+    progress("generating the 8192x57344 layer")
     x_bits = W.generate(WORKLOAD)
     M, K = x_bits.shape
     n = M * K
@@ -395,6 +402,7 @@ def main():
             if events is not None:
                 events[i][1].record()
 
+    progress("step: warm-up and timed steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -408,6 +416,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    progress("beside the step: dequantize, layout, NVFP4, blocked scales, GEMM")
     # beside the step: dequantize of the step's codes, the transposed layout
     # of the layer, and the GEMM that consumes quantized operands
     deq_out = torch.empty_like(x)
@@ -493,6 +502,7 @@ def main():
     del gc
 
     # measured ceilings on the layer's bytes
+    progress("ceilings")
     ceilings = measure_ceilings(CL, x, copy_dst)
     copy_gbps = ceilings["copy"]["GBps"]
     for e in extras:
@@ -563,6 +573,7 @@ def main():
         "outside_step": extras,
     }
     if not args.no_cpu:
+        progress("CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(x_bits, rots, args.cpu_rows, args.cpu_rows_1t)
     else:
         out["cpu_baseline"] = None

@@ -140,6 +140,32 @@ def test_rot128_qdq_work_unit_edges(mx, fmt, shape):
     _qdq_band(mx, fmt, x, W.hadamard_rotation(128), 128)
 
 
+@pytest.mark.parametrize("shape", [(1, 128), (16, 2048), (1931, 2176)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_rot128_lane_kernel_grid_edges(mx, shape):
+    """Quantize (MX) and NVFP4 at r = 128 run on a persistent grid of one
+    wave per workgroup, 8 per CU, whose waves take interleaved 16-block
+    tiles: one partial tile, exactly 16 tiles, and 2052 tiles (the last one
+    partial) so that the first waves take a second tile.  MX quantize and
+    NVFP4 QDQ and quantize of every row within the band of the oracle."""
+    import torch
+    from _bandcheck import check_nv
+    x = W.random_bf16(shape, seed=shape[0] + 17)
+    R = W.hadamard_rotation(128)
+    xg, Rg = to_gpu_bf16(x), to_gpu_bf16(R)
+    results = []
+    for fmt in (E2M1, E4M3):
+        codes, scales = mx.mx_quantize(fmt, xg, rot=Rg)
+        results.append({"fmt": fmt, "codes": bits_of(codes), "scales": bits_of(scales)})
+    check_mx(x, R, 128, results, what=f"lane kernel {shape}")
+    g = 448.0 * 6.0 / float(np.abs(W.bf16_bits_to_f32(x)).max())
+    gt = torch.tensor([g], dtype=torch.float32, device="cuda")
+    c, sc = mx.mx_nvfp4_quantize(xg, gt, rot=Rg)
+    q = mx.mx_nvfp4_qdq(xg, gt, rot=Rg)
+    torch.cuda.synchronize()
+    check_nv(x, R, 128, float(np.float32(g)), [{"codes": bits_of(c), "scales": bits_of(sc)}, {"deq": bits_of(q)}],
+             what=f"lane kernel nvfp4 {shape}")
+
+
 @pytest.mark.parametrize("fmt", [E2M1, E4M3])
 @pytest.mark.parametrize("r,shape", [(16, (6, 96)), (16, (10, 160)), (32, (6, 96)), (32, (10, 160)), (16, (5, 96))],
                          ids=lambda v: str(v))
