@@ -853,19 +853,18 @@ static void dispatch_rb(int dtype, const void *src, const void *rot, int r, void
 }
 
 // Which bf16 rotations run on the lane-owned kernels of rotl.hip: r = 128
-// for MX quantize with row-major scales and for NVFP4.  Measured on MI355X
-// against the kernels here, on the 8192 x 57344 layer, same box and run:
-// MX quantize MXFP4 / MXFP8 3% / 2% faster, NVFP4 QDQ and quantize 5%
-// faster; MX QDQ within the noise of the short-lived 16-block kernel (kept);
-// at r <= 64 slower (the full 128-wide contraction where the 64-element
-// blocks here do a half or less); with blocked scales slower (more
-// scattered byte stores).
+// for MX quantize (row-major scales, or blocked scales written by whole
+// units) and for NVFP4.  Measured on MI355X against the kernels here, on the
+// 8192 x 57344 layer, same box and run: MX quantize MXFP4 / MXFP8 3% / 2%
+// faster, NVFP4 QDQ and quantize 5% faster; MX QDQ within the noise of the
+// short-lived 16-block kernel (kept); at r <= 64 slower (the full 128-wide
+// contraction where the 64-element blocks here do a half or less).
 static bool lanes_for(int fmt, int op, int r, const BlockedScales *bl) {
 #if defined(MXQDQ_ROT_STAGED)
   (void)fmt, (void)op, (void)r, (void)bl;
   return false;
 #else
-  return r == 128 && bl == nullptr && (op == OP_QUANT || fmt == 2);
+  return r == 128 && (op == OP_QUANT || fmt == 2);
 #endif
 }
 

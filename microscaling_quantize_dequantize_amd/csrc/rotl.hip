@@ -64,12 +64,14 @@ constexpr int TB = 16;                       // blocks per tile
 constexpr int TILE_ELEMS = TB * RB;          // 2048
 constexpr int TILE_BYTES = TILE_ELEMS * 2;   // 4 KiB of bf16
 constexpr int RSRC_FLAGS = 0x00020000;       // raw 32-bit buffer
+constexpr unsigned OOB_OFFSET = 0x80000000u;  // a buffer offset past every record
 #ifndef RL_AUX
 #define RL_AUX 2                             // cache policy of the tile loads: non-temporal
 #endif
 
 template <int NB> struct Lds {
-  static constexpr int bytes = WAVES * NB * TILE_BYTES;
+  static constexpr int ring = WAVES * NB * TILE_BYTES;
+  static constexpr int bytes = ring + WAVES * 256;  // + one blocked scale unit per wave
 };
 
 #define RL_LDS(p) ((__attribute__((address_space(3))) void *)(p))
@@ -138,24 +140,112 @@ __device__ __forceinline__ void piece_nv(const float v[8], const NvTensor &t, un
 
 // Vector-memory operations of one tile's stores, for the exact waits: QDQ 4
 // (one 16-byte piece per lane and block set); quantize 4 code stores and the
-// scale bytes (MX row-major: 1; blocked: 4 byte stores; NVFP4: 4 byte stores).
+// scale bytes (MX row-major: 1; blocked: 4 byte stores; NVFP4: 4 byte
+// stores; blocked by units: none, and one unit store every 4th tile, left
+// out of the count, which only makes the waits wait longer).
 template <int FMT, int OP, int SL> constexpr int stores_per_tile() {
-  return OP == OP_QDQ ? 4 : (FMT == 2 || SL == 1 ? 8 : 5);
+  return OP == OP_QDQ ? 4 : (SL == 2 ? 4 : (FMT == 2 || SL == 1 ? 8 : 5));
+}
+
+// Orders a wave's LDS accesses around an exchange between its lanes.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// SL 2 epilogue of tile `tile` (tile % 4 is its place in its unit, whose 4
+// tiles the wave takes in a row): codes by buffer stores (rows past M and a
+// second column block past K are dropped), scale bytes into the wave's unit
+// buffer, and after the unit's last tile the unit itself.  Tile block b is
+// row r0 + b / 2, column block b % 2; lane (p, n) of set i holds piece n of
+// block 4i + p: row r0 + 2i + p / 2, columns c0 + 128 (p % 2) + 8n ..
+template <int FMT>
+__device__ __forceinline__ void unit_tile_epilogue(const f32x4 (&acc)[8], int64_t tile, int64_t K,
+                                                   int64_t col_pairs, const BlockedScales &bl,
+                                                   uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                   int64_t n_elem, uint8_t *unit_bytes, int lane) {
+  const int p = lane >> 4, n = lane & 15;
+  const int64_t u = tile >> 2;
+  const int q = (int)(tile & 3);
+  const int64_t r0 = (u / col_pairs) * 32 + 8 * q, c0 = (u % col_pairs) * 256;
+  const bool second = c0 + RB < K;  // the unit's second column block exists
+  if (q == 0) {
+    ((unsigned *)unit_bytes)[lane] = 0x7F7F7F7Fu;  // padding scale 2^0
+    wave_lds_fence();
+  }
+  constexpr int CB = FMT == 0 ? 1 : 2;  // code bytes per 2 elements
+  const int64_t e0 = r0 * K + c0;
+  int64_t left = (n_elem - e0) * CB / 2;
+  const int64_t span = (7 * K + 2 * RB) * CB / 2;
+  left = left < 0 ? 0 : (left > span ? span : left);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(left > 0 ? codes + e0 * CB / 2 : codes, (short)0,
+                                                                      (int)left, RSRC_FLAGS);
+  const bool lane_cols = second || (p & 1) == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[8];
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) v[jt] = acc[jt][i];
+    unsigned sb;
+    float sc;
+    u32x2 c;
+    piece_codes<FMT>(v, sb, sc, c);
+    unsigned off = lane_cols ? (unsigned)((((2 * i + (p >> 1)) * K) + RB * (p & 1) + 8 * n) * CB / 2) : OOB_OFFSET;
+    opaque_offset(off);
+    if (FMT == 0) {
+      if (sb == 255u) c.x = 0u;
+      __builtin_amdgcn_raw_buffer_store_b32(c.x, rc, off, 0, RL_AUX);
+    } else {
+      if (sb == 255u) c = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
+      __builtin_amdgcn_raw_buffer_store_b64(c, rc, off, 0, RL_AUX);
+    }
+    // group n/4 of this block at unit position: word 32 h + row, byte g8 / 2,
+    // g8 = 4 (p % 2) + n / 4 the group within the unit, h = g8 % 2
+    const int row = 8 * q + 2 * i + (p >> 1), g8 = 4 * (p & 1) + (n >> 2);
+    if ((n & 3) == 0 && lane_cols && r0 + 2 * i + (p >> 1) < bl.rows)
+      unit_bytes[4 * (32 * (g8 & 1) + row) + (g8 >> 1)] = (uint8_t)sb;
+  }
+  if (q == 3) {
+    wave_lds_fence();
+    const unsigned w = ((const unsigned *)unit_bytes)[lane];
+    __builtin_nontemporal_store(w, (unsigned *)(scales + u * 256) + lane);
+    wave_lds_fence();
+  }
 }
 
 // The wave's tiles, once its B fragments are in registers.  FMT: 0 MXFP4,
 // 1 MXFP8, 2 NVFP4 (g: the per-tensor multiplier; NVFAST selects the
 // division-free quotients).  SL (MX quantize): 0 row-major scales, 1 the
-// blocked layout `bl`.
+// blocked layout `bl` with a byte store per group, 2 the blocked layout by
+// whole units (below).
+//
+// SL 2: a blocked scale unit covers 32 rows x 8 groups (256 columns), so
+// its tiles are not 16 consecutive blocks but 8 rows of two 128-column
+// blocks: unit u = (row block u / cb, column pair u % cb), cb = ceil(K/256),
+// and its 4 tiles q = 0..3 take rows 8q .. 8q+7 of it (UNIT = 4, so a wave
+// does a unit's tiles in a row).  The wave gathers the unit's 256 scale bytes in LDS (starting from
+// the padding value 127) and writes them with one coalesced 256-byte store.
+// Loads past the tensor read as zero and stores past it are dropped by the
+// buffer resources, so every tile issues the same stores.
 template <int FMT, int OP, int SL, int NB, int UNIT, bool NVFAST>
 __device__ __forceinline__ void rot_lanes_tiles(const uint16_t *__restrict__ src, const u32x4 (&rb)[8][4],
                                                 uint16_t *__restrict__ dst, uint8_t *__restrict__ codes,
                                                 uint8_t *__restrict__ scales, int64_t n_elem,
-                                                const BlockedScales &bl, float g, uint8_t *ring, int lane,
-                                                int64_t wave_id, int64_t n_waves) {
+                                                const BlockedScales &bl, float g, uint8_t *ring,
+                                                uint8_t *unit_bytes, int lane, int64_t wave_id, int64_t n_waves) {
   const int p = lane >> 4, n = lane & 15;
-  const int64_t n_tiles = (n_elem + TILE_ELEMS - 1) / TILE_ELEMS;
+  static_assert(SL != 2 || (UNIT == 4 && OP == OP_QUANT && FMT != 2), "unit tiles: MX quantize, 4 per unit");
+  const int64_t K = SL == 2 ? bl.groups * 32 : 0;
+  const int64_t col_pairs = SL == 2 ? bl.gblocks : 0;
+  const int64_t n_tiles = SL == 2 ? 4 * ((bl.rows + 31) / 32) * col_pairs : (n_elem + TILE_ELEMS - 1) / TILE_ELEMS;
   const int64_t n_units = (n_tiles + UNIT - 1) / UNIT;
+  // SL 2: first row and column of a tile, and whether its columns exist
+  auto unit_tile = [&](int64_t tile, int64_t &r0, int64_t &c0) -> bool {
+    const int64_t u = tile >> 2, q = tile & 3;
+    r0 = (u / col_pairs) * 32 + 8 * q;
+    c0 = (u % col_pairs) * 256;
+    return c0 + RB < K;  // whether the second column block exists
+  };
   NvTensor nvt{};
   if constexpr (FMT == 2) nvt = nv_tensor<NVFAST>(g);
 
@@ -166,16 +256,36 @@ __device__ __forceinline__ void rot_lanes_tiles(const uint16_t *__restrict__ src
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int b = 4 * q + (lane >> 4);
-    voff[q] = (unsigned)(256 * b + 16 * ((lane & 15) ^ b));
+    // SL 2: block b is row b / 2, column block b % 2 of the tile
+    const unsigned base = SL == 2 ? (unsigned)(2 * (K * (b >> 1) + RB * (b & 1))) : 256u * b;
+    voff[q] = base + 16 * ((lane & 15) ^ b);
   }
   auto tile_of = [&](int64_t k) -> int64_t { return (wave_id + (k / UNIT) * n_waves) * UNIT + k % UNIT; };
   auto issue = [&](int64_t k) {
     const int64_t tile = tile_of(k);
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src, n_elem, tile < n_tiles ? tile : n_tiles);
+    __amdgpu_buffer_rsrc_t rs;
+    bool second = true;
+    if constexpr (SL == 2) {
+      int64_t r0 = 0, c0 = 0;
+      second = unit_tile(tile, r0, c0);
+      const int64_t e0 = r0 * K + c0;
+      int64_t left = tile < n_tiles ? n_elem - e0 : 0;
+      const int64_t span = 7 * K + 2 * RB;
+      left = left < 0 ? 0 : (left > span ? span : left);
+      rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(left > 0 ? src + e0 : src), (short)0,
+                                             (int)(left * 2), RSRC_FLAGS);
+    } else {
+      rs = tile_rsrc(src, n_elem, tile < n_tiles ? tile : n_tiles);
+    }
     uint8_t *buf = ring + (int)(k % NB) * TILE_BYTES;
+    // SL 2 without a second column block: its lanes (odd block) read zeros
+    const bool drop = SL == 2 && !second && ((lane >> 4) & 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, RL_LDS(buf + 1024 * q), 16, voff[q], 0, 0, RL_AUX);
+    for (int q = 0; q < 4; ++q) {
+      unsigned off = drop ? OOB_OFFSET : voff[q];
+      opaque_offset(off);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, RL_LDS(buf + 1024 * q), 16, off, 0, 0, RL_AUX);
+    }
   };
   // A fragment reads: lane (p, m = n) takes block beta(m), piece 4 kb + p
   const int bm = 4 * (n & 3) + (n >> 2);
@@ -213,6 +323,10 @@ __device__ __forceinline__ void rot_lanes_tiles(const uint16_t *__restrict__ src
                                                           __builtin_bit_cast(bf16x8, rb[jt][kb]), acc[jt], 0, 0, 0);
     }
     if (tile >= n_tiles) continue;  // wave-uniform: nothing to store
+    if constexpr (SL == 2) {
+      unit_tile_epilogue<FMT>(acc, tile, K, col_pairs, bl, codes, scales, n_elem, unit_bytes, lane);
+      continue;
+    }
     const int64_t e_tile = tile * TILE_ELEMS;
     const bool full = e_tile + TILE_ELEMS <= n_elem;
     unsigned sbw[4];
@@ -306,7 +420,7 @@ void k_rot_lanes(const uint16_t *__restrict__ src, const uint16_t *__restrict__ 
   const int64_t n_waves = (int64_t)gridDim.x * WAVES;
   const int64_t wave_id = (int64_t)blockIdx.x * WAVES + wave;
   if (SL == 1) write_blocked_pads(scales, bl, (int64_t)blockIdx.x * THREADS + threadIdx.x,
-                                  (int64_t)gridDim.x * THREADS);
+                                  (int64_t)gridDim.x * THREADS);  // SL 2 writes whole units, padding included
 
   // R into registers: the 8 B fragments of k step kb (jt = 0..7) of lane
   // (p, n) are the 8 x 8 sub-block of Reff at rows 32 kb + 8p .. +7 and
@@ -336,17 +450,18 @@ void k_rot_lanes(const uint16_t *__restrict__ src, const uint16_t *__restrict__ 
     }
 
   uint8_t *ring = lds + wave * NB * TILE_BYTES;
+  uint8_t *unit_bytes = lds + Lds<NB>::ring + wave * 256;
   if constexpr (FMT == 2) {
     const float g = *gp;
     if (nv_fast(g))
-      rot_lanes_tiles<FMT, OP, SL, NB, UNIT, true>(src, rb, dst, codes, scales, n_elem, bl, g, ring, lane, wave_id,
-                                                   n_waves);
+      rot_lanes_tiles<FMT, OP, SL, NB, UNIT, true>(src, rb, dst, codes, scales, n_elem, bl, g, ring, unit_bytes,
+                                                   lane, wave_id, n_waves);
     else
-      rot_lanes_tiles<FMT, OP, SL, NB, UNIT, false>(src, rb, dst, codes, scales, n_elem, bl, g, ring, lane,
-                                                    wave_id, n_waves);
+      rot_lanes_tiles<FMT, OP, SL, NB, UNIT, false>(src, rb, dst, codes, scales, n_elem, bl, g, ring, unit_bytes,
+                                                    lane, wave_id, n_waves);
   } else {
-    rot_lanes_tiles<FMT, OP, SL, NB, UNIT, true>(src, rb, dst, codes, scales, n_elem, bl, 0.0f, ring, lane,
-                                                 wave_id, n_waves);
+    rot_lanes_tiles<FMT, OP, SL, NB, UNIT, true>(src, rb, dst, codes, scales, n_elem, bl, 0.0f, ring, unit_bytes,
+                                                 lane, wave_id, n_waves);
   }
 }
 
@@ -395,8 +510,9 @@ hipError_t launch_rot_lanes(int fmt, int op, const void *src, const void *rot, i
     if (fmt == 0) rl::launch<0, OP_QUANT, 0, NB, rl_unit<0, OP_QUANT>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
     else rl::launch<1, OP_QUANT, 0, NB, rl_unit<1, OP_QUANT>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
   } else {
-    if (fmt == 0) rl::launch<0, OP_QUANT, 1, NB, 1>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
-    else rl::launch<1, OP_QUANT, 1, NB, 1>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
+    // blocked scales: whole units (4 tiles of 16 rows x 128 columns each)
+    if (fmt == 0) rl::launch<0, OP_QUANT, 2, NB, 4>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
+    else rl::launch<1, OP_QUANT, 2, NB, 4>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
   }
   return hipGetLastError();
 }

@@ -68,8 +68,12 @@ def test_quantize_blocked_matches_oracle(mx, fmt, shape):
 
 @pytest.mark.parametrize("fmt", [E2M1, E4M3])
 @pytest.mark.parametrize("r,shape", [(16, (77, 224)), (16, (6, 96)), (32, (33, 288)), (32, (10, 160)), (64, (45, 384)),
-                                     (128, (129, 1152))], ids=lambda v: str(v))
+                                     (128, (129, 1152)), (128, (1, 128)), (128, (31, 384)), (128, (64, 256)),
+                                     (128, (96, 2176))], ids=lambda v: str(v))
 def test_quantize_blocked_rotated_equals_rowmajor(mx, fmt, r, shape):
+    """Rotation 128 writes blocked scales by whole units of 32 rows x 256
+    columns: rows past M and a last unit with only 128 columns of K are
+    padding (2^0), as the re-blocked row-major scales have them."""
     import torch
     M, K = shape
     x = to_gpu_bf16(W.random_bf16((M, K), seed=7 * r + M))

@@ -301,3 +301,50 @@ def test_e4m3_chunk_window(mx):
     c = mx.mx_matmul(E2M1, gpu_u8(a[None]), gpu_u8(s), gpu_u8(a[None]), gpu_u8(s), K, dtype=torch.float32)
     torch.cuda.synchronize()
     assert float(c.cpu()[0, 0]) == 36.25
+
+
+def test_accumulation_across_steps_is_faithful(mx):
+    """How the matrix core adds each 64-deep k-step to its fp32 accumulator,
+    on one output (E2M1, groups of 32 with their own scales): the step's sum
+    is added rounded to nearest-even (a tail 1 or 2 bits below the ulp of the
+    running sum rounds up above a midpoint, a tie goes to even, a step just
+    below a midpoint rounds down) but within a short window of guard bits and
+    with no sticky bit: a tail 7 bits below the ulp is dropped, so 1 + 2^-24 +
+    2^-30 rounds down to 1 where round-to-nearest gives 1 + 2^-23.  The same
+    holds across a 256-deep slice and for negative sums; within a step the
+    sum of 1 and 2^-23 is exact.  Each addition is therefore faithful (error
+    below one ulp of its result), not round-to-nearest: the GEMM bound's
+    accumulation term is K * 2^-23 * sum |a_k b_k|."""
+    import torch
+    K = 512
+    CODE = {1.0: 2, 0.5: 1, -1.0: 0xA}  # E2M1 codes
+
+    def dot(items):
+        """items: (group, element, a value, b value, a scale byte, b scale
+        byte); every other element is zero and other scales are 2^0."""
+        a = np.zeros(K // 2, np.uint8)
+        b = np.zeros(K // 2, np.uint8)
+        sa = np.full((1, K // 32), 127, np.uint8)
+        sb = np.full((1, K // 32), 127, np.uint8)
+        for g, e, va, vb, xa, xb in items:
+            k = 32 * g + e
+            a[k // 2] |= CODE[va] << (4 * (k % 2))
+            b[k // 2] |= CODE[vb] << (4 * (k % 2))
+            sa[0, g], sb[0, g] = xa, xb
+        c = mx.mx_matmul(E2M1, gpu_u8(a[None]), gpu_u8(sa), gpu_u8(b[None]), gpu_u8(sb), K, dtype=torch.float32)
+        torch.cuda.synchronize()
+        return float(c.cpu()[0, 0])
+
+    u = 2.0 ** -24
+    one, mone = (0, 0, 1.0, 1.0, 127, 127), (0, 0, -1.0, 1.0, 127, 127)
+    assert dot([one, (1, 0, 1.0, 1.0, 115, 116)]) == 1 + 2 * u                 # in one step: exact
+    for g in (2, 8):                                                           # the next step; the next slice
+        half = (g, 0, 1.0, 1.0, 115, 115)                                      # 2^-24
+        quarter = (g, 1, 0.5, 1.0, 115, 115)                                   # 2^-25
+        tiny, neg_tiny = (g + 1, 0, 1.0, 1.0, 112, 112), (g + 1, 0, -1.0, 1.0, 112, 112)  # +-2^-30
+        assert dot([one, half, quarter]) == 1 + 2 * u, g                       # 1.5 ulp/2 above 1: up
+        assert dot([one, half]) == 1.0, g                                      # tie, even: stays
+        assert dot([one, (g, 0, -1.0, 1.0, 115, 115), neg_tiny]) == 1 - u, g   # below 1: nearest
+        assert dot([one, half, tiny]) == 1.0, g                                # 2^-30 dropped: not nearest
+        assert dot([mone, (g, 0, -1.0, 1.0, 115, 115), neg_tiny]) == -1.0, g   # the same for negatives
+        assert dot([one, (1, 0, 1.0, 1.0, 115, 116), half]) == 1 + 4 * u, g   # tie, odd: to even (up)
