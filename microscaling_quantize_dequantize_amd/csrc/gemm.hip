@@ -24,18 +24,23 @@
 // every row (four E2M1 or two E4M3 k-steps: 2048 matrix-core cycles per wave
 // either way).
 //
-// Data path (measured on gfx950: with one workgroup per CU, loads of whole
-// 128-byte row segments stream about twice as fast as 64-byte ones, and LDS
-// writes from registers run at a third of the LDS read rate):
+// Data path (measured on gfx950 with GEMM-shaped slices, one workgroup per
+// CU: loads of whole 128-byte row segments stream at 91 GB/s per CU, 64-byte
+// ones at 57 GB/s whatever the number in flight; LDS writes from registers
+// run at a third of the LDS read rate):
 //   codes go from global memory straight into LDS (buffer loads with an LDS
 //   destination), one wave instruction per 8 rows x 128 bytes, into one of
 //   two static LDS slots; rows past the operands and the K tail read as zero
 //   through the buffer resource;
 //   the fragments of each k-step are read from LDS while the matrix cores run
 //   the previous k-step;
-//   one barrier per slice, placed before its last k-step, publishes the next
-//   slice (loaded during this one), so that the last k-step's MFMAs overlap
-//   the reads of the next slice's first fragments.
+//   two barriers per slice: the first, once every wave has read the slice's
+//   last fragments, frees its slot for the slice after next; the second,
+//   before the last 8 MFMAs, publishes the next slice, so that those MFMAs
+//   overlap the reads of the next slice's first fragments;
+//   the loads are paced, one per 64 cycles per wave, between the two
+//   barriers, after the second and through the next slice's first k-steps
+//   (see "Pacing" below).
 // LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by (row/2)%8,
 // which keeps the 16-lane fragment reads free of bank conflicts.
 #include <type_traits>
@@ -58,6 +63,47 @@ constexpr int DMA_W = TILE / 1024 / 4;                // 1 KB loads per wave per
 constexpr unsigned OOB = 0x80000000u;                 // a buffer offset past every record
 constexpr int RSRC_FLAGS = 0x00020000;                // raw 32-bit buffer
 static_assert(BM == BN && BM == GT, "one thread per row stages the row-major scales");
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// Pacing of a slice's loads.  A wave that issues loads with an LDS
+// destination faster than the address unit takes them (16 cycles per 1 KB
+// instruction, shared by the CU's four waves) stalls at issue, and its
+// matrix-core work with it; so each wave issues at most one per 64 cycles:
+// one per two E2M1 MFMAs, one per E4M3 MFMA.  Measured on gfx950 with
+// GEMM-shaped slices (64 KB per CU): loads alone take 0.78 us per slice and
+// MFMAs alone 1.05 us; a burst of each wave's 16 loads ahead of its 64 MFMAs
+// takes 1.5 us, the same loads issued by other waves 1.15 us.
+#ifndef MXG_JA4
+#define MXG_JA4 4
+#endif
+#ifndef MXG_JB4
+#define MXG_JB4 4
+#endif
+#ifndef MXG_JS04
+#define MXG_JS04 8
+#endif
+#ifndef MXG_JA8
+#define MXG_JA8 8
+#endif
+#ifndef MXG_JB8
+#define MXG_JB8 8
+#endif
+#ifndef MXG_SPLIT4
+#define MXG_SPLIT4 1
+#endif
+
+// the number of n events, spread evenly over m slots, that fall in slot k
+__device__ __forceinline__ constexpr int spread(int k, int n, int m) { return ((k + 1) * n) / m - (k * n) / m; }
+
+// a scheduling group of n (0..4) vector-memory instructions
+__device__ __forceinline__ void sched_vmem(int n) {
+  if (n == 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+  else if (n == 2) __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
+  else if (n == 3) __builtin_amdgcn_sched_group_barrier(0x010, 3, 0);
+  else if (n >= 4) __builtin_amdgcn_sched_group_barrier(0x010, 4, 0);
+}
 
 template <int FMT>
 struct GemmShape {
@@ -86,9 +132,10 @@ static __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p
 // Scale layouts: SL 0 row-major bytes; SL 1 blocked (a wave's words for its
 // 8 tiles and one 256-deep k-span are two 1 KB loads straight into LDS);
 // SL 2 row-major with groups % NG == 0, so a row's NG bytes of a slice are
-// whole aligned dwords; SL 3 (E2M1) row-major with groups % 16 == 0 and
-// 16-byte aligned scales, loaded by 16-byte spans of two slices (the
-// group-parity split of the LDS-loaded forms is done when a slice starts).
+// whole aligned dwords; SL 3 row-major with groups % 16 == 0 and 16-byte
+// aligned scales, loaded by 16-byte spans of 16 groups (two E2M1 slices or
+// four E4M3 slices; the group-parity split of the LDS-loaded forms is done
+// when a slice starts).
 template <int FMT, int OUT, int SL, bool TAIL>
 __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                                                  const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
@@ -100,24 +147,37 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   constexpr int NWB = SL == 1 ? 4 * (TI + TJ) * 64 : 4;   // blocked words per slot
   constexpr int NWR = SL == 1 || SL == 3 ? 4 : 2 * (BM + BN);  // row-major words per slot
   // Row-major scales:
-  //  - E2M1, SL 3 (SPAN): 16 bytes of every row (16 groups, two slices)
-  //    straight into LDS, loaded every other slice into one of two span
-  //    buffers;
+  //  - SL 3 (SPAN): 16 bytes of every row (16 groups: two E2M1 slices, four
+  //    E4M3 slices) straight into LDS, one load per row and span into one of
+  //    two span buffers.  A load of scales covers 64 rows, one line each, so
+  //    its address-unit time is several code loads'; spans take the fewest;
   //  - E4M3, SL 2 (SDMA): one dword per row and slice straight into LDS
   //    (9% faster than through registers);
   //  - otherwise (SREG) through registers: E2M1 at SL 2 (its two dwords per
   //    row and slice would take twice the LDS-destination loads of one
   //    8-byte load per thread, measured 6% slower) and the byte loads of
   //    SL 0.
-  static_assert(SL != 3 || FMT == 0, "spans are for E2M1");
   constexpr bool SPAN = SL == 3;
+  constexpr int SPLC = 16 / NG;  // slices per span
   constexpr bool SDMA = SL == 2 && FMT == 1;
   constexpr bool SREG = SL == 0 || (SL == 2 && FMT == 0);
-  // E4M3 publishes each slice with two barriers (see the slice loop): its
-  // two k-steps per slice let the slot be refilled a quarter slice earlier
-  // (8% faster); E2M1's four k-steps gain an eighth, less than the second
-  // barrier costs (1% slower).
-  constexpr bool SPLIT = FMT == 1;
+  // Each slice is published with two barriers (see the slice loop), so that
+  // a slot starts taking the loads of the slice after next as soon as its
+  // last fragments have been read: E4M3 2.12 -> 1.95 ms (row-major scales)
+  // and 1.79 -> 1.69 ms (blocked) when the loads went out in one burst; with
+  // paced loads, E2M1 gains 3-4% over one barrier.
+  constexpr bool SPLIT = FMT == 1 || MXG_SPLIT4;
+  // a slice's load jobs: the code loads, then the scale loads that travel
+  // with it; JA are issued between the two barriers (SPLIT), JB after the
+  // publishing barrier, JS0 and JS1 during the next slice's k-steps 0 and 1
+  constexpr int NJ = 2 * DMA_W + (SL == 1 || SDMA ? 2 : 0);
+  constexpr int JA0 = !SPLIT ? 0 : FMT == 0 ? MXG_JA4 : MXG_JA8, JA = JA0 < NJ ? JA0 : NJ;
+  constexpr int JB0 = FMT == 0 ? MXG_JB4 : MXG_JB8, JB = JB0 < NJ - JA ? JB0 : NJ - JA;
+  constexpr int JS0 = FMT == 0 ? (NJ - JA - JB < MXG_JS04 ? NJ - JA - JB : MXG_JS04) : NJ - JA - JB;
+  constexpr int JS1 = NJ - JA - JB - JS0;
+  static_assert(JA >= 0 && JB >= 0 && JS0 >= 0 && JS1 >= 0 && (NS == 4 || JS1 == 0), "job schedule");
+  // register scale loads issued with the slice after next (SREG)
+  constexpr int NSREG = !(SL == 0 || (SL == 2 && FMT == 0)) ? 0 : SL == 2 ? 2 : 2 * NG;
   static_assert(DMA_W == 8, "16 code loads per wave and slice");
   constexpr int NSP = SPAN ? (BM + BN) * 16 : 16;       // span buffer bytes
   __shared__ __attribute__((aligned(1024))) uint8_t sm0[SLOT], sm1[SLOT];
@@ -162,53 +222,61 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
     dvoff[i] = (unsigned)(row * rb + 16 * dchunk[i]);
   }
   auto slot_of = [&](auto Pc) -> uint8_t * { return decltype(Pc)::value ? sm1 : sm0; };
-  // load slice ks into slot P (prefetches past the last slice re-read it)
-  auto load_slice = [&](auto Pc, int ks) {
+  // The loads of slice ks into slot P, as NJ jobs in issue order: job j <
+  // 2*DMA_W is code load j/2 of operand j%2 (A, B), then the slice's scale
+  // loads (blocked words, or the SDMA dwords).  Jobs [LO, HI) are issued;
+  // prefetches past the last slice re-read it.
+  auto load_jobs = [&](auto Pc, int ks, auto LO, auto HI) {
+    constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
     uint8_t *slot = slot_of(Pc);
     const int kq = ks < nslices ? ks : nslices - 1;
     const int kb0 = kq * RB;
 #pragma unroll
-    for (int i = 0; i < DMA_W; ++i) {
-      unsigned off = dvoff[i];
-      if constexpr (TAIL) {
-        // the last slice of a K that is not a whole number of slices:
-        // chunks past the row read as zero
-        off = 16 * dchunk[i] < rb - kb0 ? off : OOB;
-        opaque_offset(off);
+    for (int jb = lo; jb < hi; ++jb) {
+      if (jb < 2 * DMA_W) {
+        const int i = jb >> 1;
+        unsigned off = dvoff[i];
+        if constexpr (TAIL) {
+          // the last slice of a K that is not a whole number of slices:
+          // chunks past the row read as zero
+          off = 16 * dchunk[i] < rb - kb0 ? off : OOB;
+          opaque_offset(off);
+        }
+        uint8_t *dst = slot + (4 * i + wave) * 1024 + (jb & 1) * TILE;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((jb & 1) ? rB : rA, MX_LDS(dst), 16, off, kb0, 0, 0);
+      } else if constexpr (SL == 1) {
+        // blocked words of the slice's 256-deep span: lane L takes words
+        // 4(L%16)..4(L%16)+3 of tile L/16 (A tiles, then B tiles)
+        unsigned *wb = decltype(Pc)::value ? wb1 : wb0;
+        const int span = (kq * BK) >> 8;
+        if (jb == 2 * DMA_W) {
+          const unsigned va = (unsigned)(((wm >> 5) + (lane >> 4)) * gblocks * 256 + 16 * (lane & 15));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, MX_LDS(wb + wave * (TI + TJ) * 64), 16, va, span * 256, 0, 0);
+        } else {
+          const unsigned vb = (unsigned)(((wn >> 5) + (lane >> 4)) * gblocks * 256 + 16 * (lane & 15));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, MX_LDS(wb + (wave * (TI + TJ) + TI) * 64), 16, vb,
+                                                   span * 256, 0, 0);
+        }
+      } else if constexpr (SDMA) {
+        // the slice's NG = 4 scale bytes of every row, straight into LDS as
+        // [row][4]: wave w takes rows 64w..64w+63 of each operand, a dword
+        // per lane
+        static_assert(NG == 4, "one dword per row");
+        unsigned *wr = decltype(Pc)::value ? wr1 : wr0;
+        const unsigned voff = (unsigned)((64 * wave + lane) * groups);
+        if (jb == 2 * DMA_W) __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, MX_LDS(wr + 64 * wave), 4, voff, kq * NG, 0, 0);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, MX_LDS(wr + BM + 64 * wave), 4, voff, kq * NG, 0, 0);
       }
-      uint8_t *dst = slot + (4 * i + wave) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, MX_LDS(dst), 16, off, kb0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, MX_LDS(dst + TILE), 16, off, kb0, 0, 0);
-    }
-    if constexpr (SL == 1) {
-      // blocked words of the slice's 256-deep span: lane L takes words
-      // 4(L%16)..4(L%16)+3 of tile L/16 (A tiles, then B tiles)
-      unsigned *wb = decltype(Pc)::value ? wb1 : wb0;
-      const int span = (kq * BK) >> 8;
-      const unsigned va = (unsigned)(((wm >> 5) + (lane >> 4)) * gblocks * 256 + 16 * (lane & 15));
-      const unsigned vb = (unsigned)(((wn >> 5) + (lane >> 4)) * gblocks * 256 + 16 * (lane & 15));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, MX_LDS(wb + wave * (TI + TJ) * 64), 16, va, span * 256, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, MX_LDS(wb + (wave * (TI + TJ) + TI) * 64), 16, vb, span * 256,
-                                               0, 0);
-    } else if constexpr (SDMA) {
-      // the slice's NG = 4 scale bytes of every row, straight into LDS as
-      // [row][4]: wave w takes rows 64w..64w+63 of each operand, a dword per
-      // lane
-      static_assert(NG == 4, "one dword per row");
-      unsigned *wr = decltype(Pc)::value ? wr1 : wr0;
-      const unsigned voff = (unsigned)((64 * wave + lane) * groups);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rAs, MX_LDS(wr + 64 * wave), 4, voff, kq * NG, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rBs, MX_LDS(wr + BM + 64 * wave), 4, voff, kq * NG, 0, 0);
     }
   };
 
-  // ---- row-major E2M1 scales by 16-byte spans (SPAN): span j holds groups
-  // 16j..16j+15 of every row, i.e. slices 2j and 2j+1, in buffer j % 2 as
-  // [row][16]; wave w loads rows 64w..64w+63 of each operand, a row per
-  // lane.  The launch takes this path only when the groups of a row are a
-  // multiple of 16, so no span reaches past its row -------------------------
+  // ---- row-major scales by 16-byte spans (SPAN): span j holds groups
+  // 16j..16j+15 of every row, i.e. slices SPLC*j .. SPLC*j + SPLC-1, in
+  // buffer j % 2 as [row][16]; wave w loads rows 64w..64w+63 of each
+  // operand, a row per lane.  The launch takes this path only when the
+  // groups of a row are a multiple of 16, so no span reaches past its row ---
   auto load_span = [&](int j) {
-    const int nspans = nslices / 2;
+    const int nspans = nslices / SPLC;
     const int jq = j < nspans ? j : nspans - 1;  // past the end: re-read the last span, unused
     uint8_t *d = wsp[j & 1];
     const unsigned voff = (unsigned)((64 * wave + lane) * groups + 16 * jq);
@@ -284,12 +352,15 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   // overlaps), and its value: byte t is the scale of k-step t for lanes of
   // half h.
   using Word = typename std::conditional<SDMA || SPAN, u32x2, unsigned>::type;
-  auto read_word = [&](auto Pc, int f, int ks) -> Word {
+  // (H: the slice's phase ks % SPLC in its span, for SPAN)
+  auto read_word = [&](auto Pc, auto Hc, int f, int ks) -> Word {
     if constexpr (SPAN) {
-      // slice ks = 2j + P: bytes 8P..8P+7 of the row in span buffer j % 2
-      const uint8_t *b = wsp[(ks >> 1) & 1];
-      return *(const u32x2 *)(b + 16 * (f < TI ? wm + 32 * f + r : BM + wn + 32 * (f - TI) + r) +
-                              8 * decltype(Pc)::value);
+      // slice ks = SPLC*j + H: bytes NG*H .. NG*H + NG-1 of the row in span
+      // buffer j % 2
+      constexpr int H = decltype(Hc)::value;
+      const uint8_t *b = wsp[(ks / SPLC) & 1] + 16 * (f < TI ? wm + 32 * f + r : BM + wn + 32 * (f - TI) + r);
+      if constexpr (FMT == 0) return *(const u32x2 *)(b + 8 * H);
+      else return u32x2{*(const unsigned *)(b + 4 * H), 0u};
     } else if constexpr (SL == 1) {
       const unsigned *wb = decltype(Pc)::value ? wb1 : wb0;
       return wb[(wave * (TI + TJ) + f) * 64 + lane];
@@ -343,8 +414,8 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   RowScales rs_next{};  // row-major scales of the slice after next (SREG)
 
   if (nslices > 0) {
-    load_slice(P0{}, 0);
-    load_slice(P1{}, 1);
+    load_jobs(P0{}, 0, IC<0>{}, IC<NJ>{});
+    load_jobs(P1{}, 1, IC<0>{}, IC<JA + JB>{});  // the rest during slice 0
     if constexpr (SPAN) {
       load_span(0);
       load_span(1);
@@ -357,14 +428,20 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
 #pragma unroll
     for (int f = 0; f < TI + TJ; ++f) {
       fr[0][f] = read_frag(P0{}, f, 0);
-      wd[f] = read_word(P0{}, f, 0);
+      wd[f] = read_word(P0{}, IC<0>{}, f, 0);
     }
   }
 
-  // one k-slice ks in slot P (P = ks % 2)
-  auto slice = [&](auto Pc, int ks) {
+  // one k-slice ks in slot P (P = ks % 2), at phase H = ks % SPLC of its
+  // span (SPAN)
+  auto slice = [&](auto Pc, auto Hc, int ks) {
     constexpr int P = decltype(Pc)::value;
     using Q = std::integral_constant<int, P ^ 1>;
+    constexpr int H = decltype(Hc)::value;
+    using HN = IC<(H + 1) % SPLC>;  // the next slice's phase
+    // SPAN: once the last slice of span j is published, span j+2 goes into
+    // the buffer of span j, whose words every wave has read
+    constexpr bool SPAN_LOAD = SPAN && H == SPLC - 1;
     // scale byte of k-step t: blocked E4M3 slices are half a span
     auto byte_of = [](auto T) { return std::integral_constant<int, (SL == 1 && FMT == 1 ? 2 * P : 0) + decltype(T)::value>{}; };
     // the slice's scale words (wd is refilled with the next slice's before
@@ -375,13 +452,17 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
     // k-steps 0..NS-2, each reading the next step's fragments
     auto step = [&](auto T) {
       constexpr int t = decltype(T)::value;
+      constexpr int lo = JA + JB + (t == 0 ? 0 : JS0), cnt = t == 0 ? JS0 : t == 1 ? JS1 : 0;
       mfma(byte_of(T), fr[t & 1], wcur);
 #pragma unroll
       for (int f = 0; f < TI + TJ; ++f) fr[(t + 1) & 1][f] = read_frag(Pc, f, t + 1);
+      // the rest of the next slice's loads, into the other slot, paced
+      if constexpr (cnt > 0) load_jobs(Q{}, ks + 1, IC<lo>{}, IC<lo + cnt>{});
 #pragma unroll
       for (int k = 0; k < TI * TJ; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, FMT == 0 ? 1 : 2, 0);  // fragment reads
+        sched_vmem(spread(k, cnt, TI * TJ));
       }
     };
     step(std::integral_constant<int, 0>{});
@@ -404,18 +485,17 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
 #pragma unroll
       for (int f = 0; f < TI + TJ; ++f) {
         fr[0][f] = read_frag(Q{}, f, 0);
-        wd[f] = read_word(Q{}, f, ks + 1);
+        wd[f] = read_word(Q{}, HN{}, f, ks + 1);
       }
-      load_slice(Pc, ks + 2);
-      // SPAN: once slice 2j+1 is published, span j+2 goes into the buffer
-      // of span j, whose last words (slice 2j+1's) every wave has read
-      if constexpr (SPAN && P == 1) load_span((ks + 1) / 2 + 1);
+      load_jobs(Pc, ks + 2, IC<0>{}, IC<JB>{});
+      if constexpr (SPAN_LOAD) load_span((ks + 1) / SPLC + 1);
       if constexpr (SREG) rs_next = load_row_scales(ks + 2);
+      constexpr int nv = JB + (SPAN_LOAD ? 2 : 0) + NSREG;
 #pragma unroll
       for (int k = 0; k < AFTER; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TI + TJ) / AFTER * (FMT == 0 ? 1 : 2), 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x010, 3, 0);  // loads of the slice after next
+        sched_vmem(spread(k, nv, AFTER));  // loads of the slice after next
       }
     } else {
       // Two barriers.  A (LDS only): every wave has read this slice's last
@@ -430,34 +510,50 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       // give the new loads no time at all.
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if constexpr (SREG) rs_next = load_row_scales(ks + 2);  // before the loads: waiting for it must not wait for them
-      load_slice(Pc, ks + 2);
+      load_jobs(Pc, ks + 2, IC<0>{}, IC<JA>{});
       mfma(last, fr[(NS - 1) & 1], wcur, 0, TI * TJ - AFTER);
 #pragma unroll
       for (int k = 0; k < TI * TJ - AFTER; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x010, 3, 0);  // loads of the slice after next
+        sched_vmem(spread(k, JA + NSREG, TI * TJ - AFTER));  // loads of the slice after next
       }
-      asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(JA + NSREG) : "memory");
       mfma(last, fr[(NS - 1) & 1], wcur, TI * TJ - AFTER, TI * TJ);
 #pragma unroll
       for (int f = 0; f < TI + TJ; ++f) {
         fr[0][f] = read_frag(Q{}, f, 0);
-        wd[f] = read_word(Q{}, f, ks + 1);
+        wd[f] = read_word(Q{}, HN{}, f, ks + 1);
       }
+      load_jobs(Pc, ks + 2, IC<JA>{}, IC<JA + JB>{});
+      if constexpr (SPAN_LOAD) load_span((ks + 1) / SPLC + 1);
+      constexpr int nv = JB + (SPAN_LOAD ? 2 : 0);
 #pragma unroll
       for (int k = 0; k < AFTER; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TI + TJ) / AFTER * (FMT == 0 ? 1 : 2), 0);  // LDS reads
+        sched_vmem(spread(k, nv, AFTER));  // loads of the slice after next
       }
     }
   };
 
   int ks = 0;
-  for (; ks + 1 < nslices; ks += 2) {
-    slice(P0{}, ks);
-    slice(P1{}, ks + 1);
+  if constexpr (SPLC == 4 && SPAN) {
+    // E4M3 spans: a phase per slice of a span (the launch takes this path
+    // only when groups % 16 == 0, so the slices are a multiple of four)
+    for (; ks + 3 < nslices; ks += 4) {
+      slice(P0{}, IC<0>{}, ks);
+      slice(P1{}, IC<1>{}, ks + 1);
+      slice(P0{}, IC<2>{}, ks + 2);
+      slice(P1{}, IC<3>{}, ks + 3);
+    }
+  } else {
+    // the phase of a two-slice span is the slot parity
+    for (; ks + 1 < nslices; ks += 2) {
+      slice(P0{}, IC<0>{}, ks);
+      slice(P1{}, IC<1 % SPLC>{}, ks + 1);
+    }
+    if (ks < nslices) slice(P0{}, IC<0>{}, ks);
   }
-  if (ks < nslices) slice(P0{}, ks);
   // the last slice's prefetch (a re-read of the last slice, never used) is
   // still landing in LDS: drain it before the workgroup can end
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -545,12 +641,11 @@ hipError_t launch_gemm(int fmt, const uint8_t *a, const uint8_t *as, const uint8
     run_gemm_k<1>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
   } else {
     // aligned loads per row when every slice's groups line up, 16-byte spans
-    // when the groups of a row are a multiple of 16 (E2M1)
+    // when the groups of a row are a multiple of 16
     const int ng = fmt == 0 ? GemmShape<0>::NG : GemmShape<1>::NG;
     const bool aligned = (K / 32) % ng == 0 && (uintptr_t)as % 4 == 0 && (uintptr_t)bs % 4 == 0;
-    const bool spans = fmt == 0 && (K / 32) % 16 == 0 && (uintptr_t)as % 16 == 0 && (uintptr_t)bs % 16 == 0;
-    if (spans && out_dtype == 0) k_mx_gemm<0, 0, 3, false><<<grid, GT, 0, st>>>(a, as, b, bs, M, N, K, alpha, c);
-    else if (spans) k_mx_gemm<0, 1, 3, false><<<grid, GT, 0, st>>>(a, as, b, bs, M, N, K, alpha, c);
+    const bool spans = (K / 32) % 16 == 0 && (uintptr_t)as % 16 == 0 && (uintptr_t)bs % 16 == 0;
+    if (spans) run_gemm<3, false>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
     else if (aligned) run_gemm_k<2>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
     else run_gemm_k<0>(fmt, out_dtype, grid, a, as, b, bs, M, N, K, alpha, c, st);
   }
