@@ -93,18 +93,7 @@ using IC = std::integral_constant<int, N>;
 #ifndef MXG_SPLIT4
 #define MXG_SPLIT4 1
 #endif
-#ifndef MXG_RD4
-#define MXG_RD4 1
-#endif
-#ifndef MXG_RORD
-#define MXG_RORD 0
-#endif
-// the order in which a k-step's fragments are read: A0 A1 A2 A3 B0 B1 B2 B3,
-// or (RORD) A0 B0 B1 B2 B3 A1 A2 A3, which the first MFMAs (row 0 of the
-// 4 x 4 tiles) need first
-__device__ __forceinline__ constexpr int frag_order(int n) {
-  return MXG_RORD == 0 ? n : n == 0 ? 0 : n <= 4 ? TI + n - 1 : n - 4;
-}
+
 
 // the number of n events, spread evenly over m slots, that fall in slot k
 __device__ __forceinline__ constexpr int spread(int k, int n, int m) { return ((k + 1) * n) / m - (k * n) / m; }
@@ -467,18 +456,13 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       constexpr int lo = JA + JB + (t == 0 ? 0 : JS0), cnt = t == 0 ? JS0 : t == 1 ? JS1 : 0;
       mfma(byte_of(T), fr[t & 1], wcur);
 #pragma unroll
-      for (int n = 0; n < TI + TJ; ++n) {
-        const int f = frag_order(n);
-        fr[(t + 1) & 1][f] = read_frag(Pc, f, t + 1);
-      }
+      for (int f = 0; f < TI + TJ; ++f) fr[(t + 1) & 1][f] = read_frag(Pc, f, t + 1);
       // the rest of the next slice's loads, into the other slot, paced
       if constexpr (cnt > 0) load_jobs(Q{}, ks + 1, IC<lo>{}, IC<lo + cnt>{});
 #pragma unroll
       for (int k = 0; k < TI * TJ; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        if (FMT == 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // fragment reads
-        else if (MXG_RD4 == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        else if (k < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, FMT == 0 ? 1 : 2, 0);  // fragment reads
         sched_vmem(spread(k, cnt, TI * TJ));
       }
     };
@@ -488,10 +472,7 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       step(std::integral_constant<int, 2>{});
     }
     if constexpr (SREG) store_row_scales(Q{}, rs_next);
-#ifndef MXG_AFTER4
-#define MXG_AFTER4 8
-#endif
-    constexpr int AFTER = FMT == 0 ? MXG_AFTER4 : 8;  // MFMAs after the barrier that publishes the next slice
+    constexpr int AFTER = 8;  // MFMAs after the barrier that publishes the next slice
     const auto last = byte_of(std::integral_constant<int, NS - 1>{});
     if constexpr (!SPLIT) {
       // The last k-step: most of its MFMAs, then the barrier that publishes
@@ -503,8 +484,7 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       publish_lds_loads();
       mfma(last, fr[(NS - 1) & 1], wcur, TI * TJ - AFTER, TI * TJ);
 #pragma unroll
-      for (int n = 0; n < TI + TJ; ++n) {
-        const int f = frag_order(n);
+      for (int f = 0; f < TI + TJ; ++f) {
         fr[0][f] = read_frag(Q{}, f, 0);
         wd[f] = read_word(Q{}, HN{}, f, ks + 1);
       }
@@ -541,8 +521,7 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(JA + NSREG) : "memory");
       mfma(last, fr[(NS - 1) & 1], wcur, TI * TJ - AFTER, TI * TJ);
 #pragma unroll
-      for (int n = 0; n < TI + TJ; ++n) {
-        const int f = frag_order(n);
+      for (int f = 0; f < TI + TJ; ++f) {
         fr[0][f] = read_frag(Q{}, f, 0);
         wd[f] = read_word(Q{}, HN{}, f, ks + 1);
       }
