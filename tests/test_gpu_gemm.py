@@ -266,6 +266,32 @@ def test_full_size_sampled(mx, fmt):
     assert math.isfinite(float(cv.sum()))
 
 
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+def test_full_size_scale_paths_agree(mx, fmt):
+    """At 8192 x 8192 x 28672 the kernel reads row-major scales by 16-byte
+    spans (scales 16-byte aligned), by aligned dwords or 8-byte rows (4-byte
+    aligned), by bytes (any alignment), or in the blocked layout: the same
+    scale values give the same products in the same order, so every output of
+    the four runs has the same bits (the oracle bounds them in
+    test_full_size_sampled)."""
+    import torch
+    ac, as_ = full_operand(fmt, FULL_M, 700 + fmt)
+    bc, bs = full_operand(fmt, FULL_N, 800 + fmt)
+    A, B = gpu_u8(ac), gpu_u8(bc)
+    sa, sb = gpu_u8(as_), gpu_u8(bs)
+    outs = []
+    for off in (0, 4, 1):
+        outs.append(mx.mx_matmul(fmt, A, offset_copy(sa, off), B, offset_copy(sb, off), FULL_K,
+                                 dtype=torch.bfloat16))
+    ba, bb = mx.mx_scales_to_blocked(sa, FULL_K), mx.mx_scales_to_blocked(sb, FULL_K)
+    outs.append(mx.mx_matmul(fmt, A, ba, B, bb, FULL_K, dtype=torch.bfloat16, scale_layout=mx.BLOCKED))
+    torch.cuda.synchronize()
+    ref = outs[0].view(torch.int16)
+    for what, o in zip(("dwords", "bytes", "blocked"), outs[1:]):
+        same = torch.eq(o.view(torch.int16), ref)
+        assert bool(same.all()), f"{what}: {int((~same).sum())} outputs differ from the span path"
+
+
 # ---- characterisation of the matrix core's E4M3 dot-product window -----------
 
 def test_e4m3_chunk_window(mx):
