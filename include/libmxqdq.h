@@ -22,7 +22,9 @@
  *     matrix loaded at runtime, sizes 16/32/64/128): every r-element chunk x
  *     of a row (chunks start at column 0) is replaced by y = x . R, i.e.
  *     y[j] = sum_t x[t] * R[t][j], with R an r x r row-major matrix in the
- *     source dtype, products exact and accumulation in fp32.  For a symmetric
+ *     source dtype, accumulated in fp32.  bf16 sources multiply exactly (bf16
+ *     matrix cores); fp32 sources run on the fp32 matrix cores, whose
+ *     products are rounded once to fp32.  For a symmetric
  *     matrix such as the normalised Hadamard H * r^-0.5 the side does not
  *     matter.  QDQ then returns the dequantized rotated values (no inverse).
  *

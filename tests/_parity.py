@@ -2,8 +2,10 @@
 comparison, and the tolerance band of the rotated path.
 
 Rotated path bar (stated tolerance): a rotated value may differ from the
-exact one by at most beta = 1e-5 * sum_t |x[t] R[t][j]| (fp32 accumulation of
-exact products); at most 0.01% of the elements may differ from the oracle's
+exact one by at most beta = 1e-5 * sum_t |x[t] R[t][j]| (fp32 accumulation;
+the products are exact for bf16 sources and rounded once to fp32 for fp32
+sources, at most 2^-24 |x[t] R[t][j]| each, well inside beta); at most 0.01%
+of the elements may differ from the oracle's
 result, and each difference must be one that some rotated value within beta
 would produce:
   - a group's scale may be any of those the abs-max can take within the band
