@@ -417,10 +417,7 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   if (nslices > 0) {
     load_jobs(P0{}, 0, IC<0>{}, IC<NJ>{});
     load_jobs(P1{}, 1, IC<0>{}, IC<JA + JB>{});  // the rest during slice 0
-    if constexpr (SPAN) {
-      load_span(0);
-      load_span(1);
-    }
+    if constexpr (SPAN) load_span(0);  // span 1 goes out during slice 0
     if constexpr (SREG) {
       store_row_scales(P0{}, load_row_scales(0));
       rs_next = load_row_scales(1);
@@ -440,9 +437,12 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
     using Q = std::integral_constant<int, P ^ 1>;
     constexpr int H = decltype(Hc)::value;
     using HN = IC<(H + 1) % SPLC>;  // the next slice's phase
-    // SPAN: once the last slice of span j is published, span j+2 goes into
-    // the buffer of span j, whose words every wave has read
-    constexpr bool SPAN_LOAD = SPAN && H == SPLC - 1;
+    // SPAN: the first slice of span j+1 loads span j+2 into the buffer of
+    // span j, whose words every wave has read (the last of them, for span j's
+    // last slice, before the barrier that published it), paced among the
+    // MFMAs of k-step SPAN_T; span j+2 is first read a whole span later
+    constexpr bool SPAN_LOAD = SPAN && H == 0;
+    constexpr int SPAN_T = NS == 4 ? 1 : 0;
     // scale byte of k-step t: blocked E4M3 slices are half a span
     auto byte_of = [](auto T) { return std::integral_constant<int, (SL == 1 && FMT == 1 ? 2 * P : 0) + decltype(T)::value>{}; };
     // the slice's scale words (wd is refilled with the next slice's before
@@ -459,11 +459,13 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
       for (int f = 0; f < TI + TJ; ++f) fr[(t + 1) & 1][f] = read_frag(Pc, f, t + 1);
       // the rest of the next slice's loads, into the other slot, paced
       if constexpr (cnt > 0) load_jobs(Q{}, ks + 1, IC<lo>{}, IC<lo + cnt>{});
+      if constexpr (SPAN_LOAD && t == SPAN_T) load_span(ks / SPLC + 1);
+      constexpr int nv = cnt + (SPAN_LOAD && t == SPAN_T ? 2 : 0);
 #pragma unroll
       for (int k = 0; k < TI * TJ; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, FMT == 0 ? 1 : 2, 0);  // fragment reads
-        sched_vmem(spread(k, cnt, TI * TJ));
+        sched_vmem(spread(k, nv, TI * TJ));
       }
     };
     step(std::integral_constant<int, 0>{});
@@ -489,9 +491,8 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
         wd[f] = read_word(Q{}, HN{}, f, ks + 1);
       }
       load_jobs(Pc, ks + 2, IC<0>{}, IC<JB>{});
-      if constexpr (SPAN_LOAD) load_span((ks + 1) / SPLC + 1);
       if constexpr (SREG) rs_next = load_row_scales(ks + 2);
-      constexpr int nv = JB + (SPAN_LOAD ? 2 : 0) + NSREG;
+      constexpr int nv = JB + NSREG;
 #pragma unroll
       for (int k = 0; k < AFTER; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -526,8 +527,7 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
         wd[f] = read_word(Q{}, HN{}, f, ks + 1);
       }
       load_jobs(Pc, ks + 2, IC<JA>{}, IC<JA + JB>{});
-      if constexpr (SPAN_LOAD) load_span((ks + 1) / SPLC + 1);
-      constexpr int nv = JB + (SPAN_LOAD ? 2 : 0);
+      constexpr int nv = JB;
 #pragma unroll
       for (int k = 0; k < AFTER; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
