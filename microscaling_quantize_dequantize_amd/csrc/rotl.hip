@@ -500,12 +500,11 @@ hipError_t launch_rot_lanes(int fmt, int op, const void *src, const void *rot, i
   const BlockedScales none{0, 0, 0};
   const BlockedScales &b = bl ? *bl : none;
   constexpr int NB = RL_NB;
+  // QDQ at r = 128 runs on the 16-block short-lived kernel (rot.hip), which
+  // measured 4-12% faster; this kernel takes the quantize forms
+  if (op != OP_QUANT) return hipErrorInvalidValue;
   if (fmt == 2) {
-    if (op == OP_QDQ) rl::launch<2, OP_QDQ, 0, NB, rl_unit<2, OP_QDQ>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
-    else rl::launch<2, OP_QUANT, 0, NB, rl_unit<2, OP_QUANT>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
-  } else if (op == OP_QDQ) {
-    if (fmt == 0) rl::launch<0, OP_QDQ, 0, NB, rl_unit<0, OP_QDQ>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
-    else rl::launch<1, OP_QDQ, 0, NB, rl_unit<1, OP_QDQ>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
+    rl::launch<2, OP_QUANT, 0, NB, rl_unit<2, OP_QUANT>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
   } else if (bl == nullptr) {
     if (fmt == 0) rl::launch<0, OP_QUANT, 0, NB, rl_unit<0, OP_QUANT>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
     else rl::launch<1, OP_QUANT, 0, NB, rl_unit<1, OP_QUANT>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
