@@ -142,11 +142,12 @@ def test_rot128_qdq_work_unit_edges(mx, fmt, shape):
 
 @pytest.mark.parametrize("shape", [(1, 128), (16, 2048), (1931, 2176)], ids=lambda s: f"{s[0]}x{s[1]}")
 def test_rot128_lane_kernel_grid_edges(mx, shape):
-    """Quantize (MX) and NVFP4 at r = 128 run on a persistent grid of one
+    """Quantize (MX and NVFP4) at r = 128 runs on a persistent grid of one
     wave per workgroup, 8 per CU, whose waves take interleaved 16-block
-    tiles: one partial tile, exactly 16 tiles, and 2052 tiles (the last one
-    partial) so that the first waves take a second tile.  MX quantize and
-    NVFP4 QDQ and quantize of every row within the band of the oracle."""
+    tiles, and NVFP4 QDQ on short-lived workgroups of 8 tiles per wave: one
+    partial tile, exactly 16 tiles, and 2052 tiles (the last one partial) so
+    that the first waves take a second tile.  MX quantize and NVFP4 QDQ and
+    quantize of every row within the band of the oracle."""
     import torch
     from _bandcheck import check_nv
     x = W.random_bf16(shape, seed=shape[0] + 17)
