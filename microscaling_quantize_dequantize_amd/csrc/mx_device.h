@@ -78,10 +78,23 @@ __device__ __forceinline__ unsigned clamp_bf16x2(unsigned w, unsigned c2) {
   return (w & 0x80008000u) | __builtin_bit_cast(unsigned, m);
 }
 
-// Clamp an fp32 magnitude to c, keeping the sign.
-__device__ __forceinline__ float clamp_f32(float y, float c) {
-  float m = __builtin_fminf(__builtin_fabsf(y), c);
-  return __builtin_copysignf(m, y);
+// Clamp an fp32 value to [-c, c] (c > 0): one v_med3_f32.  For a NaN y the
+// result is unspecified; every caller replaces the outputs of a group whose
+// abs-max is NaN.
+__device__ __forceinline__ float clamp_f32(float y, float c) { return __builtin_amdgcn_fmed3f(y, -c, c); }
+
+// Bits of max |v[i]| over N fp32 values, with the IEEE 754-2019 maximum
+// (a NaN operand gives a NaN): gfx950's v_maximum3_f32 takes two new values
+// per instruction with the absolute value as a source modifier.  For
+// non-NaN values this equals the largest of the sign-cleared bit patterns;
+// for a NaN it is a positive NaN, exponent field 255, as that largest
+// pattern would be, so the scale steps see the same exponent either way.
+template <int N>
+__device__ __forceinline__ unsigned abs_max_bits(const float *v) {
+  float m = __builtin_fabsf(v[0]);
+#pragma unroll
+  for (int i = 1; i < N; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(v[i]));
+  return __float_as_uint(m);
 }
 
 // ---- conversions of 8 bf16 (one 16-byte piece) -------------------------

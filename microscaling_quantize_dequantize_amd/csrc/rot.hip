@@ -71,15 +71,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // the 4-element runs' codes c[q] (E2M1: 16 bits, E4M3: 32 bits).
 template <int FMT>
 __device__ __forceinline__ void group_codes(const f32x16 &acc, unsigned &sb, float &sc, unsigned c[4]) {
-  unsigned m = 0;
-#pragma unroll
-  for (int a = 0; a < 16; ++a) m = umax(m, __float_as_uint(acc[a]) & 0x7FFFFFFFu);
-  m = max_across_halves(m);
-  sb = scale_byte<FMT>(m);
-  sc = scale_operand(sb);
   float y[16];
 #pragma unroll
   for (int a = 0; a < 16; ++a) y[a] = acc[a];
+  const unsigned m = max_across_halves(abs_max_bits<16>(y));
+  sb = scale_byte<FMT>(m);
+  sc = scale_operand(sb);
   if (FMT == 1) {
     const float cl = __uint_as_float(((sb + 8u) << 23) | 0x600000u);  // 448 * 2^s
 #pragma unroll
@@ -131,10 +128,10 @@ __device__ __forceinline__ void nv_group_codes(const f32x16 &acc, const NvTensor
                                                float sbv[2], unsigned c[4]) {
 #pragma unroll
   for (int hg = 0; hg < 2; ++hg) {
-    unsigned m = 0;
+    float y[8];
 #pragma unroll
-    for (int a = 0; a < 8; ++a) m = umax(m, __float_as_uint(acc[8 * hg + a]) & 0x7FFFFFFFu);
-    m = max_across_halves(m);
+    for (int a = 0; a < 8; ++a) y[a] = acc[8 * hg + a];
+    const unsigned m = max_across_halves(abs_max_bits<8>(y));
     sb[hg] = nv_scale_byte(__uint_as_float(m) * t.c6);
     sbv[hg] = nv_scale_value(sb[hg]);
   }
@@ -480,14 +477,9 @@ __device__ __forceinline__ unsigned max_across_quarters(unsigned v) {
 // fit the registers of three waves per SIMD.
 __device__ __forceinline__ void nv16_bf16(const f32x4 &a, const f32x4 &b, const NvTensor &t, bool fast,
                                           u32x2 &oa, u32x2 &ob) {
-  unsigned ma = 0, mb = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ma = umax(ma, __float_as_uint(a[i]) & 0x7FFFFFFFu);
-    mb = umax(mb, __float_as_uint(b[i]) & 0x7FFFFFFFu);
-  }
-  ma = max_across_quarters(ma);
-  mb = max_across_quarters(mb);
+  const float fa[4] = {a[0], a[1], a[2], a[3]}, fb[4] = {b[0], b[1], b[2], b[3]};
+  const unsigned ma = max_across_quarters(abs_max_bits<4>(fa));
+  const unsigned mb = max_across_quarters(abs_max_bits<4>(fb));
   const float va = nv_scale_value(nv_scale_byte(__uint_as_float(ma) * t.c6));
   const float vb = nv_scale_value(nv_scale_byte(__uint_as_float(mb) * t.c6));
   float la, lb, ka, kb;
@@ -515,13 +507,8 @@ __device__ __forceinline__ void nv16_bf16(const f32x4 &a, const f32x4 &b, const 
 template <int FMT>
 __device__ __forceinline__ void group16_codes(const f32x4 &a, const f32x4 &b, unsigned &sb, float &sc,
                                               unsigned &ca, unsigned &cb) {
-  unsigned m = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = umax(m, __float_as_uint(a[i]) & 0x7FFFFFFFu);
-    m = umax(m, __float_as_uint(b[i]) & 0x7FFFFFFFu);
-  }
-  m = max_across_quarters(m);
+  const float ab[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  const unsigned m = max_across_quarters(abs_max_bits<8>(ab));
   sb = scale_byte<FMT>(m);
   sc = scale_operand(sb);
   float ya[4], yb[4];

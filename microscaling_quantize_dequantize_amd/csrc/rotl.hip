@@ -98,9 +98,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *src,
 // of a 32-group whose other 24 are in the 3 neighbouring lanes of its quad.
 template <int FMT>
 __device__ __forceinline__ void piece_codes(const float v[8], unsigned &sb, float &sc, u32x2 &c) {
-  unsigned m = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) m = umax(m, __float_as_uint(v[e]) & 0x7FFFFFFFu);
+  unsigned m = abs_max_bits<8>(v);
   m = umax(m, dpp<DPP_QUAD_1032>(m));
   m = umax(m, dpp<DPP_QUAD_2301>(m));
   sb = scale_byte<FMT>(m);
@@ -128,9 +126,7 @@ __device__ __forceinline__ void piece_codes(const float v[8], unsigned &sb, floa
 template <bool FAST>
 __device__ __forceinline__ void piece_nv(const float v[8], const NvTensor &t, unsigned &sb, float &sbv,
                                          unsigned &c) {
-  unsigned m = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) m = umax(m, __float_as_uint(v[e]) & 0x7FFFFFFFu);
+  unsigned m = abs_max_bits<8>(v);
   m = umax(m, dpp<DPP_QUAD_1032>(m));
   sb = nv_scale_byte(__uint_as_float(m) * t.c6);
   sbv = nv_scale_value(sb);

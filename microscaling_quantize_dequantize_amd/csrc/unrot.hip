@@ -135,8 +135,8 @@ __global__ __launch_bounds__(THREADS) void k_unrot_f32(const u32x4 *__restrict__
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t p = base + (int64_t)u * THREADS;
       const u32x4 x = w[u];
-      unsigned m = umax(umax(x.x & 0x7FFFFFFFu, x.y & 0x7FFFFFFFu),
-                        umax(x.z & 0x7FFFFFFFu, x.w & 0x7FFFFFFFu));
+      const float f[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
+      unsigned m = abs_max_bits<4>(f);
       m = umax(m, dpp<DPP_ROW_HALF_MIRROR>(m));  // lanes i and 7-i of each 8
       m = umax(m, dpp<DPP_QUAD_1032>(m));
       m = umax(m, dpp<DPP_QUAD_2301>(m));
