@@ -327,81 +327,89 @@ __device__ __forceinline__ void rot_lanes_tiles(const uint16_t *__restrict__ src
       continue;
     }
     const int64_t e_tile = tile * TILE_ELEMS;
-    const bool full = e_tile + TILE_ELEMS <= n_elem;
-    unsigned sbw[4];
+    // A tile inside the tensor stores every piece: it runs an instance of
+    // the epilogue without the per-lane bounds tests.
+    auto epilogue = [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
+      unsigned sbw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v[8];
+      for (int i = 0; i < 4; ++i) {
+        float v[8];
 #pragma unroll
-      for (int jt = 0; jt < 8; ++jt) v[jt] = acc[jt][i];
-      // piece n of block 4i + p: elements e_tile + 512 i + 8 lane
-      const int64_t e = e_tile + 512 * i + 8 * lane;
-      const bool ok = full || e < n_elem;
-      if constexpr (FMT == 2) {
-        unsigned sb, c;
-        float sbv;
-        piece_nv<NVFAST>(v, nvt, sb, sbv, c);
-        if (OP == OP_QDQ) {
-          const float kf = nv_kf<NVFAST>(nvt, sbv);
-          const u32x4 o = {nv_bf16_pair<0>(c, kf), nv_bf16_pair<1>(c, kf), nv_bf16_pair<2>(c, kf),
-                           nv_bf16_pair<3>(c, kf)};
-          if (ok) __builtin_nontemporal_store(o, (u32x4 *)(dst + e));
-        } else {
-          if (ok) __builtin_nontemporal_store(c, (unsigned *)(codes + e / 2));
-          if ((lane & 1) == 0 && ok) scales[e >> 4] = (uint8_t)sb;  // the pair's 16-group
-        }
-        continue;
-      } else {
-        unsigned sb;
-        float sc;
-        u32x2 c;
-        piece_codes<FMT>(v, sb, sc, c);
-        if (OP == OP_QDQ) {
-          u32x4 o = FMT == 0 ? bf16x8_from_fp4(c.x, sc) : bf16x8_from_fp8(c, sc);
-          if (sb == 255u) {
-            const unsigned nn = BF16_NAN | (BF16_NAN << 16);
-            o = u32x4{nn, nn, nn, nn};
-          }
-          if (ok) __builtin_nontemporal_store(o, (u32x4 *)(dst + e));
-        } else {
-          if (FMT == 0) {
-            if (sb == 255u) c.x = 0u;
-            if (ok) __builtin_nontemporal_store(c.x, (unsigned *)(codes + e / 2));
+        for (int jt = 0; jt < 8; ++jt) v[jt] = acc[jt][i];
+        // piece n of block 4i + p: elements e_tile + 512 i + 8 lane
+        const int64_t e = e_tile + 512 * i + 8 * lane;
+        const bool ok = FULL || e < n_elem;
+        if constexpr (FMT == 2) {
+          unsigned sb, c;
+          float sbv;
+          piece_nv<NVFAST>(v, nvt, sb, sbv, c);
+          if (OP == OP_QDQ) {
+            const float kf = nv_kf<NVFAST>(nvt, sbv);
+            const u32x4 o = {nv_bf16_pair<0>(c, kf), nv_bf16_pair<1>(c, kf), nv_bf16_pair<2>(c, kf),
+                             nv_bf16_pair<3>(c, kf)};
+            if (ok) __builtin_nontemporal_store(o, (u32x4 *)(dst + e));
           } else {
-            if (sb == 255u) c = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
-            if (ok) __builtin_nontemporal_store(c, (u32x2 *)(codes + e));
+            if (ok) __builtin_nontemporal_store(c, (unsigned *)(codes + e / 2));
+            if ((lane & 1) == 0 && ok) scales[e >> 4] = (uint8_t)sb;  // the pair's 16-group
           }
-          if (SL == 1) {
-            if ((lane & 3) == 0 && ok) {
-              const int64_t gf = e >> 5, row = gf / bl.groups;
-              scales[blocked_offset(row, gf - row * bl.groups, bl.gblocks)] = (uint8_t)sb;
+          continue;
+        } else {
+          unsigned sb;
+          float sc;
+          u32x2 c;
+          piece_codes<FMT>(v, sb, sc, c);
+          if (OP == OP_QDQ) {
+            u32x4 o = FMT == 0 ? bf16x8_from_fp4(c.x, sc) : bf16x8_from_fp8(c, sc);
+            if (sb == 255u) {
+              const unsigned nn = BF16_NAN | (BF16_NAN << 16);
+              o = u32x4{nn, nn, nn, nn};
             }
+            if (ok) __builtin_nontemporal_store(o, (u32x4 *)(dst + e));
           } else {
-            // lanes 16p .. 16p+15 hold the 4 groups of block 4i + p: after
-            // two row rotations every lane of the row holds their 4 bytes
-            unsigned w = sb << (8 * ((lane >> 2) & 3));
-            w |= dpp<DPP_ROW_ROR4>(w);
-            w |= dpp<DPP_ROW_ROR8>(w);
-            sbw[i] = w;
+            if (FMT == 0) {
+              if (sb == 255u) c.x = 0u;
+              if (ok) __builtin_nontemporal_store(c.x, (unsigned *)(codes + e / 2));
+            } else {
+              if (sb == 255u) c = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
+              if (ok) __builtin_nontemporal_store(c, (u32x2 *)(codes + e));
+            }
+            if (SL == 1) {
+              if ((lane & 3) == 0 && ok) {
+                const int64_t gf = e >> 5, row = gf / bl.groups;
+                scales[blocked_offset(row, gf - row * bl.groups, bl.gblocks)] = (uint8_t)sb;
+              }
+            } else {
+              // lanes 16p .. 16p+15 hold the 4 groups of block 4i + p: after
+              // two row rotations every lane of the row holds their 4 bytes
+              unsigned w = sb << (8 * ((lane >> 2) & 3));
+              w |= dpp<DPP_ROW_ROR4>(w);
+              w |= dpp<DPP_ROW_ROR8>(w);
+              sbw[i] = w;
+            }
           }
         }
       }
-    }
-    if (FMT != 2 && OP == OP_QUANT && SL == 0) {
-      // lane 16p + i (i < 4) stores the 4 scale bytes of block 4i + p
-      const int i = lane & 15;
-      const unsigned w = i == 0 ? sbw[0] : (i == 1 ? sbw[1] : (i == 2 ? sbw[2] : sbw[3]));
-      const int64_t g0 = e_tile / 32 + 16 * i + 4 * p;  // first group of block 4i + p
-      if (i < 4) {
-        if (full || 32 * g0 + RB <= n_elem) {
-          *(unsigned *)(scales + g0) = w;
-        } else {
-          // the tensor ends inside this block (r < 128): its groups up to the end
-          for (int q = 0; q < 4; ++q)
-            if (32 * (g0 + q) < n_elem) scales[g0 + q] = (uint8_t)(w >> (8 * q));
+      if (FMT != 2 && OP == OP_QUANT && SL == 0) {
+        // lane 16p + i (i < 4) stores the 4 scale bytes of block 4i + p
+        const int i = lane & 15;
+        const unsigned w = i == 0 ? sbw[0] : (i == 1 ? sbw[1] : (i == 2 ? sbw[2] : sbw[3]));
+        const int64_t g0 = e_tile / 32 + 16 * i + 4 * p;  // first group of block 4i + p
+        if (i < 4) {
+          if (FULL || 32 * g0 + RB <= n_elem) {
+            *(unsigned *)(scales + g0) = w;
+          } else {
+            // the tensor ends inside this block (r < 128): its groups up to the end
+            for (int q = 0; q < 4; ++q)
+              if (32 * (g0 + q) < n_elem) scales[g0 + q] = (uint8_t)(w >> (8 * q));
+          }
         }
       }
-    }
+    };
+    if (e_tile + TILE_ELEMS <= n_elem)
+      epilogue(std::true_type{});
+    else
+      epilogue(std::false_type{});
   }
   wait_vm<0>();  // no load may land in LDS after the workgroup has left it
 }
