@@ -52,7 +52,12 @@
  *
  * Non-finite input (outside every accuracy contract): a group holding NaN or
  * Inf gets scale byte 0xFF, E4M3 codes 0x7F (E2M1 codes 0x0), and
- * dequantized values NaN.
+ * dequantized values NaN.  With a rotation the group is the rotated one, and
+ * a NaN or Inf input reaches every output of the block the kernel rotates it
+ * in (products with Inf and sums of opposite infinities give NaN, and so do
+ * the zeros of a block-diagonal matrix): bf16 sources rotate blocks of
+ * max(r, 64) elements when M*K is a multiple of 64 (else max(r, 32)), fp32
+ * sources blocks of max(r, 32); each group of such a block is non-finite.
  */
 #ifndef LIBMXQDQ_H
 #define LIBMXQDQ_H

@@ -918,25 +918,18 @@ static void dispatch_rb(int dtype, const void *src, const void *rot, int r, void
 }
 
 // Which bf16 rotations run on the lane-owned kernels of rotl.hip: r = 128
-// for MX quantize (row-major scales, or blocked scales written by whole
-// units) and for NVFP4.  Measured on MI355X against the kernels here, on the
+// quantize, MX (row-major scales, or blocked scales written by whole units)
+// and NVFP4.  Measured on MI355X against the kernels here, on the
 // 8192 x 57344 layer, same box and run: MX quantize MXFP4 / MXFP8 3% / 2%
-// faster, NVFP4 QDQ and quantize 5% faster; MX QDQ within the noise of the
-// short-lived 16-block kernel (kept); at r <= 64 slower (the full 128-wide
+// faster, NVFP4 quantize 5% faster.  QDQ at r = 128, MX and NVFP4, runs on
+// the short-lived 16-block kernel, which measured faster than the lane-owned
+// one; at r <= 64 the lane-owned kernel is slower (the full 128-wide
 // contraction where the 64-element blocks here do a half or less).
-static bool lanes_for(int fmt, int op, int r, const BlockedScales *bl) {
-#if defined(MXQDQ_ROT_STAGED)
-  (void)fmt, (void)op, (void)r, (void)bl;
-  return false;
-#else
-  (void)bl, (void)fmt;
-  return r == 128 && op == OP_QUANT;
-#endif
-}
+static bool lanes_for(int op, int r) { return r == 128 && op == OP_QUANT; }
 
 hipError_t launch_nv_rot(int op, const void *src, const void *rot, int r, void *dst, uint8_t *codes,
                          uint8_t *scales, const float *gp, int64_t n, hipStream_t st) {
-  if (lanes_for(2, op, r, nullptr)) return launch_rot_lanes(2, op, src, rot, r, dst, codes, scales, n, st, nullptr, gp);
+  if (lanes_for(op, r)) return launch_rot_lanes(2, op, src, rot, r, dst, codes, scales, n, st, nullptr, gp);
   const int rb = staged_rb(r, n, nullptr);
   if (op == OP_QDQ) {
     if (rb == 32) run_staged<2, OP_QDQ, 32>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
@@ -952,7 +945,7 @@ hipError_t launch_nv_rot(int op, const void *src, const void *rot, int r, void *
 
 hipError_t launch_rot(int fmt, int op, int dtype, const void *src, const void *rot, int r, void *dst,
                       uint8_t *codes, uint8_t *scales, int64_t n, hipStream_t st, const BlockedScales *bl) {
-  if (dtype == 0 && op != OP_ROTATE && lanes_for(fmt, op, r, bl))
+  if (dtype == 0 && op != OP_ROTATE && lanes_for(op, r))
     return launch_rot_lanes(fmt, op, src, rot, r, dst, codes, scales, n, st, bl);
   if (op == OP_ROTATE) {
     dispatch_rb<0, OP_ROTATE>(dtype, src, rot, r, dst, codes, scales, n, st, nullptr);

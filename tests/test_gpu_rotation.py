@@ -245,3 +245,82 @@ def test_fp32_source_rotated(mx, fmt, r):
     out = mx.mx_qdq(fmt, to_gpu_f32(x), rot=to_gpu_f32(Pm))
     torch.cuda.synchronize()
     assert_bits_equal(bits_of(out), oracle.qdq(fmt, x, Pm, r), "f32 permutation")
+
+
+def _spread_mask(nonfinite, block):
+    """Groups [M, K/32] and elements [M, K] of every `block`-element block of a
+    row that holds a non-finite input."""
+    M, K = nonfinite.shape
+    bad = nonfinite.reshape(M, K // block, block).any(axis=2)
+    return np.repeat(bad, block // 32, axis=1), np.repeat(bad, block, axis=1)
+
+
+@pytest.mark.parametrize("r", RS)
+def test_nonfinite_inputs_rotated(mx, r):
+    """NaN and Inf inputs through every rotated bf16 kernel.  The kernels
+    rotate blocks of max(r, 64) elements here (r = 16 and 32 as a
+    block-diagonal 64 x 64 matrix whose zeros turn an Inf into NaN), so every
+    group of such a block is non-finite: scale byte 0xFF, codes 0x7F (E4M3) or
+    0x0 (E2M1), dequantized NaN.  The oracle's non-finite groups are the
+    r-chunks' own, a subset; outside the marked blocks an exact rotation (a
+    signed permutation) must match the oracle bit for bit, and a Hadamard
+    rotation must leave no group non-finite."""
+    import torch
+    x = no_negative_zero(W.generate("c5a", rows=(0, 64))[:, :4096])
+    x[0, 5] = 0x7FC0      # NaN
+    x[3, 300] = 0x7F80    # +Inf
+    x[7, 1000] = 0xFF80   # -Inf and +Inf in one chunk
+    x[7, 1001] = 0x7F80
+    x[20, 2047] = 0x7F80  # the last element of a 128-block
+    x[63, 4095] = 0xFFC0  # a negative NaN, the tensor's last element
+    M, K = x.shape
+    gbad, ebad = _spread_mask((x & 0x7FFF) >= 0x7F80, max(r, 64))
+    rng = np.random.default_rng(700 + r)
+    P = np.zeros((r, r))
+    P[np.arange(r), rng.permutation(r)] = rng.choice([-1.0, 1.0], size=r)
+    xg = to_gpu_bf16(x)
+    for name, R in (("permutation", bf16_exact(P)), ("hadamard", W.hadamard_rotation(r))):
+        Rg = to_gpu_bf16(R)
+        for fmt in (E2M1, E4M3):
+            nan_code = 0x7F if fmt == E4M3 else 0x0
+            out = mx.mx_qdq(fmt, xg, rot=Rg)
+            codes, scales = mx.mx_quantize(fmt, xg, rot=Rg)
+            bcodes, blocked = mx.mx_quantize_blocked(fmt, xg, rot=Rg)
+            torch.cuda.synchronize()
+            tag = f"r={r} {name} fmt{fmt}"
+            s, o = bits_of(scales), bits_of(out)
+            c = unpack_codes(fmt, bits_of(codes), K)
+            assert np.array_equal(s == 0xFF, gbad), f"non-finite groups {tag}"
+            assert np.all(c[ebad] == nan_code), f"non-finite codes {tag}"
+            assert np.array_equal((o & 0x7FFF) > 0x7F80, ebad), f"NaN outputs {tag}"
+            assert_bits_equal(bits_of(bcodes), bits_of(codes), f"blocked codes {tag}")
+            assert_bits_equal(bits_of(blocked), oracle.scales_to_blocked(s, K), f"blocked scales {tag}")
+            if name == "permutation":
+                c_ref, s_ref = oracle.quantize(fmt, x, R, r, threads=THREADS)
+                assert np.all(gbad[s_ref == 0xFF]), f"oracle non-finite groups inside the blocks {tag}"
+                assert_bits_equal(s[~gbad], s_ref[~gbad], f"scales {tag}")
+                assert_bits_equal(c[~ebad], unpack_codes(fmt, c_ref, K)[~ebad], f"codes {tag}")
+                o_ref = oracle.qdq(fmt, x, R, r, threads=THREADS)
+                assert_bits_equal(o[~ebad], o_ref[~ebad], f"qdq {tag}")
+
+
+@pytest.mark.parametrize("r", RS)
+def test_nonfinite_inputs_rotated_fp32(mx, r):
+    """fp32 sources rotate in blocks of max(r, 32) elements; the same rule."""
+    import torch
+    x = W.random_f32((16, 1024), seed=40 + r)
+    x[0, 5] = np.nan
+    x[3, 300] = np.inf
+    x[7, 600] = -np.inf
+    x[15, 1023] = np.nan
+    gbad, ebad = _spread_mask(~np.isfinite(x), max(r, 32))
+    rng = np.random.default_rng(800 + r)
+    P = np.zeros((r, r), dtype=np.float32)
+    P[np.arange(r), rng.permutation(r)] = rng.choice([-1.0, 1.0], size=r)
+    for fmt in (E2M1, E4M3):
+        out = mx.mx_qdq(fmt, to_gpu_f32(x), rot=to_gpu_f32(P))
+        torch.cuda.synchronize()
+        o = bits_of(out)
+        assert np.array_equal((o & 0x7FFFFFFF) > 0x7F800000, ebad), f"NaN outputs r={r} fmt{fmt}"
+        o_ref = oracle.qdq(fmt, x, P, r).view(np.uint32)
+        assert_bits_equal(o[~ebad], o_ref[~ebad], f"f32 permutation r={r} fmt{fmt}")

@@ -224,6 +224,20 @@ def test_nonfinite_groups(mx):
         nan_ref = (ref & 0x7FFF) > 0x7F80
         assert np.array_equal((o & 0x7FFF) > 0x7F80, nan_ref)
         assert np.array_equal(o[~nan_ref], ref[~nan_ref])
+    xf = W.random_f32((4, 128), seed=6)
+    xf[0, 3] = np.inf
+    xf[1, 40] = np.nan
+    xf[2, 70] = -np.inf
+    xf[3, 127] = -np.nan
+    for fmt in (E2M1, E4M3):
+        out = mx.mx_qdq(fmt, to_gpu_f32(xf))
+        torch.cuda.synchronize()
+        o = bits_of(out)
+        ref = oracle.qdq(fmt, xf).view(np.uint32)
+        nan_ref = (ref & 0x7FFFFFFF) > 0x7F800000
+        assert nan_ref.sum() == 4 * 32, "the four non-finite groups"
+        assert np.array_equal((o & 0x7FFFFFFF) > 0x7F800000, nan_ref)
+        assert np.array_equal(o[~nan_ref], ref[~nan_ref])
 
 
 def test_side_stream(mx):
