@@ -56,8 +56,9 @@
  * a NaN or Inf input reaches every output of the block the kernel rotates it
  * in (products with Inf and sums of opposite infinities give NaN, and so do
  * the zeros of a block-diagonal matrix): bf16 sources rotate blocks of
- * max(r, 64) elements when M*K is a multiple of 64 (else max(r, 32)), fp32
- * sources blocks of max(r, 32); each group of such a block is non-finite.
+ * max(r, 64) elements when M*K is a multiple of 64 (for blocked scales:
+ * when K is) and max(r, 32) otherwise, fp32 sources blocks of max(r, 32);
+ * each group of such a block is non-finite.
  */
 #ifndef LIBMXQDQ_H
 #define LIBMXQDQ_H
