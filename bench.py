@@ -19,7 +19,7 @@ duration, against 8 TB/s.
 
 Beside the step:
   - measured ceilings: a 16-byte streaming copy, read-only and write-only
-    kernel (bench_ceiling.hip, built outside the library; the best of three
+    kernel (bench_ceiling.hip, built outside the library; the best of six
     launch shapes each) and the runtime's device-to-device copy, all on the
     layer's bytes; every kernel also reports its fraction of the copy
     ceiling;
@@ -194,9 +194,9 @@ def ceiling_lib():
         raise SystemExit("bench_ceiling.so is missing: run `python __graft_entry__.py build` first")
     L = ctypes.CDLL(path)
     vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint
-    L.ceil_copy.argtypes = [vp, vp, i64, i32, vp]
-    L.ceil_read.argtypes = [vp, i64, vp, u32, i32, vp]
-    L.ceil_write.argtypes = [vp, i64, u32, i32, vp]
+    L.ceil_copy.argtypes = [vp, vp, i64, i32, i32, vp]
+    L.ceil_read.argtypes = [vp, i64, vp, u32, i32, i32, vp]
+    L.ceil_write.argtypes = [vp, i64, u32, i32, i32, vp]
     for f in (L.ceil_copy, L.ceil_read, L.ceil_write):
         f.restype = i32
     return L
@@ -209,8 +209,9 @@ def _stream_ptr():
 
 def measure_ceilings(L, x, copy_dst):
     """Best GB/s of the copy, read-only and write-only kernels over the
-    launch shapes (1, 2 or 4 pieces per thread), and of the runtime's
-    device-to-device copy, each on the bytes of x."""
+    launch shapes (64, 128 or 256 threads per workgroup; 1, 2 or 4 pieces
+    per thread), and of the runtime's device-to-device copy, each on the
+    bytes of x."""
     import torch
     nbytes = x.numel() * x.element_size()
     sink = torch.zeros(64, dtype=torch.int32, device=x.device)
@@ -220,24 +221,25 @@ def measure_ceilings(L, x, copy_dst):
             raise RuntimeError(f"ceiling kernel returned {rc}")
 
     kinds = {
-        "copy": (lambda u: check(L.ceil_copy(x.data_ptr(), copy_dst.data_ptr(), nbytes, u, _stream_ptr())),
+        "copy": (lambda t, u: check(L.ceil_copy(x.data_ptr(), copy_dst.data_ptr(), nbytes, t, u, _stream_ptr())),
                  2 * nbytes),
-        "read": (lambda u: check(L.ceil_read(x.data_ptr(), nbytes, sink.data_ptr(), 0x9E3779B9, u, _stream_ptr())),
+        "read": (lambda t, u: check(L.ceil_read(x.data_ptr(), nbytes, sink.data_ptr(), 0x9E3779B9, t, u,
+                                                _stream_ptr())),
                  nbytes),
-        "write": (lambda u: check(L.ceil_write(copy_dst.data_ptr(), nbytes, 0x3F803F80, u, _stream_ptr())),
+        "write": (lambda t, u: check(L.ceil_write(copy_dst.data_ptr(), nbytes, 0x3F803F80, t, u, _stream_ptr())),
                   nbytes),
     }
     out = {}
     for kind, (fn, b) in kinds.items():
         best = None
-        for u in (1, 2, 4):
-            fn(u)
-            avg, mn = timed(lambda: fn(u), 10)
+        for t, u in ((64, 1), (64, 2), (128, 1), (256, 1), (256, 2), (256, 4)):
+            fn(t, u)
+            avg, mn = timed(lambda: fn(t, u), 10)
             gbps = b / (avg * 1e-3) / 1e9
             if best is None or gbps > best[0]:
-                best = (gbps, u, avg)
-        out[kind] = {"GBps": round(best[0], 1), "pieces_per_thread": best[1], "avg_us": round(best[2] * 1e3, 2),
-                     "bytes": int(b)}
+                best = (gbps, t, u, avg)
+        out[kind] = {"GBps": round(best[0], 1), "threads": best[1], "pieces_per_thread": best[2],
+                     "avg_us": round(best[3] * 1e3, 2), "bytes": int(b)}
     for _ in range(2):
         copy_dst.copy_(x)
     avg, _ = timed(lambda: copy_dst.copy_(x), 10)
@@ -537,7 +539,7 @@ def main():
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
     def flush():
-        if CL.ceil_write(flush_buf.data_ptr(), flush_buf.numel(), 0, 1, _stream_ptr()) != 0:
+        if CL.ceil_write(flush_buf.data_ptr(), flush_buf.numel(), 0, 256, 1, _stream_ptr()) != 0:
             raise RuntimeError("flush write failed")
 
     config_rows, config_ratios = time_configs(mx, W, flush, copy_gbps)

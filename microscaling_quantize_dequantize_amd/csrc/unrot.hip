@@ -11,10 +11,11 @@
 // u16 max on sign-cleared bits) and then across the 4 lanes with two DPP
 // quad permutations; no LDS is touched.
 //
-// Launch shape (measured on MI355X, 8192 x 57344 bf16): small blocks of 128
-// threads, one block per 128*UNROLL pieces and no persistent loop, stream
-// HBM best -- QDQ with one piece per thread, quantize with two.  The grid
-// is capped only for inputs beyond 2^22 blocks, which then loop.
+// Launch shape (measured on MI355X, 8192 x 57344 bf16): small blocks, one
+// block per THREADS*UNROLL pieces and no persistent loop, stream HBM best --
+// QDQ with 64 threads and one piece per thread, quantize with 128 threads
+// and two.  The grid is capped only for inputs beyond 2^22 blocks, which
+// then loop.
 #include "launch.h"
 #include "mx_device.h"
 
@@ -232,7 +233,13 @@ static unsigned grid_for(int64_t n_pieces, int64_t per_block) {
 }
 
 // Launch shapes: threads per block and pieces per thread.
-constexpr int QDQ_T = 128, QDQ_U = 1;
+// bf16 QDQ runs one-wave blocks: a copy-shaped stream (16 bytes in and 16
+// out per lane) measured 2% faster with 64-thread blocks than with 128 or
+// 256 (MXFP4 QDQ on the 8192 x 57344 layer 288 -> 281 us, MXFP8 285 -> 282
+// us, same-process A/B), while quantize and dequantize, whose streams are
+// mostly reads or mostly writes, measured 1-10% slower with them.
+constexpr int QDQ_T = 64, QDQ_U = 1;
+constexpr int F32_T = 128, F32_U = 1;
 constexpr int QNT_T = 128, QNT_U = 2;
 constexpr int DEQ_T = 128;
 template <int DT> constexpr int deq_unroll() { return DT == 0 ? 2 : 1; }
@@ -242,9 +249,9 @@ hipError_t launch_unrot(int fmt, int op, int dtype, const void *src, void *dst, 
   const u32x4 *s = (const u32x4 *)src;
   if (dtype == 1) {  // fp32, QDQ only
     const int64_t np = n / 4;
-    const unsigned g = grid_for(np, QDQ_T * QDQ_U);
-    if (fmt == 0) k_unrot_f32<0, QDQ_T, QDQ_U><<<g, QDQ_T, 0, stream>>>(s, (u32x4 *)dst, np);
-    else k_unrot_f32<1, QDQ_T, QDQ_U><<<g, QDQ_T, 0, stream>>>(s, (u32x4 *)dst, np);
+    const unsigned g = grid_for(np, F32_T * F32_U);
+    if (fmt == 0) k_unrot_f32<0, F32_T, F32_U><<<g, F32_T, 0, stream>>>(s, (u32x4 *)dst, np);
+    else k_unrot_f32<1, F32_T, F32_U><<<g, F32_T, 0, stream>>>(s, (u32x4 *)dst, np);
     return hipGetLastError();
   }
   const int64_t np = n / 8;
