@@ -26,10 +26,10 @@ hipError_t launch_rot(int fmt, int op, int dtype, const void *src, const void *r
                       void *dst, uint8_t *codes, uint8_t *scales, int64_t n, hipStream_t stream,
                       const BlockedScales *bl = nullptr);
 
-// bf16 source, any rotation size, quantize (op OP_QUANT; anything else
-// returns hipErrorInvalidValue): the lane-owned kernels of rotl.hip.  fmt 0
-// MXFP4, 1 MXFP8 (bl: blocked scales, or nullptr for row-major), 2 NVFP4 (g:
-// device pointer to the per-tensor multiplier).
+// bf16 source, any rotation size: the lane-owned kernels of rotl.hip.  fmt
+// 0 MXFP4 and 1 MXFP8, quantize only (op OP_QUANT; anything else returns
+// hipErrorInvalidValue; bl: blocked scales, or nullptr for row-major), 2
+// NVFP4, QDQ or quantize (g: device pointer to the per-tensor multiplier).
 hipError_t launch_rot_lanes(int fmt, int op, const void *src, const void *rot, int r, void *dst, uint8_t *codes,
                             uint8_t *scales, int64_t n, hipStream_t stream, const BlockedScales *bl,
                             const float *g = nullptr);

@@ -32,8 +32,6 @@
 // outputs go the opposite way.  Pieces are placed with an XOR swizzle of
 // their column so that both the linear and the per-block accesses are free
 // of bank conflicts.
-#include <type_traits>
-
 #include "launch.h"
 #include "mx_device.h"
 
@@ -451,8 +449,7 @@ __attribute__((amdgpu_waves_per_eu(StagedCfg<RB>::resident * THREADS / 256))) vo
 //   accumulator jt: y[block n][j = 16jt + 4p + i], i = 0..3.
 // The 32-group g is jt 2g and 2g+1: lane l holds its elements 4p..4p+3
 // ("run a") and 16+4p..16+4p+3 ("run b"), and the group spans lanes n,
-// n+16, n+32, n+48 (two lane swaps reduce the abs-max).  For NVFP4, run a
-// is a quarter of 16-group 2g and run b of 2g+1.
+// n+16, n+32, n+48 (two lane swaps reduce the abs-max).  MX formats only.
 // LDS: a tile is 16 blocks x 16 pieces of 16 bytes; piece c of block n sits
 // at slot 16n + (c ^ n), so the fragment reads (16 lanes, one block each,
 // same c) and the coalesced accesses (16 lanes, one block's 16 pieces) are
@@ -465,41 +462,6 @@ __device__ __forceinline__ int slot16(int n, int c) { return 16 * n + (c ^ n); }
 __device__ __forceinline__ unsigned max_across_quarters(unsigned v) {
   auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
   return max_across_halves(umax(r[0], r[1]));
-}
-
-// The NVFP4 QDQ of a lane's two runs in the 16x16 layout: run a (4 values)
-// belongs to one 16-group and run b to the next, each spread over lanes n,
-// n+16, n+32 and n+48; the same steps as the other NVFP4 kernels: the
-// group's E4M3 scale from its abs-max, codes of x * (g / scale), values
-// codes * (scale / g) rounded to bf16.  fast (wave-uniform): g is in the
-// range of the division-free quotients (nv_mul); the test is taken per
-// group rather than by a second instance of the tile loop, which would not
-// fit the registers of three waves per SIMD.
-__device__ __forceinline__ void nv16_bf16(const f32x4 &a, const f32x4 &b, const NvTensor &t, bool fast,
-                                          u32x2 &oa, u32x2 &ob) {
-  const float fa[4] = {a[0], a[1], a[2], a[3]}, fb[4] = {b[0], b[1], b[2], b[3]};
-  const unsigned ma = max_across_quarters(abs_max_bits<4>(fa));
-  const unsigned mb = max_across_quarters(abs_max_bits<4>(fb));
-  const float va = nv_scale_value(nv_scale_byte(__uint_as_float(ma) * t.c6));
-  const float vb = nv_scale_value(nv_scale_byte(__uint_as_float(mb) * t.c6));
-  float la, lb, ka, kb;
-  if (fast) {
-    la = nv_mul<true>(t, va);
-    lb = nv_mul<true>(t, vb);
-    ka = nv_kf<true>(t, va);
-    kb = nv_kf<true>(t, vb);
-  } else {
-    la = nv_mul<false>(t, va);
-    lb = nv_mul<false>(t, vb);
-    ka = nv_kf<false>(t, va);
-    kb = nv_kf<false>(t, vb);
-  }
-  unsigned ca = fp4_from_f32x2<0>(0u, a[0] * la, a[1] * la, 1.0f);
-  ca = fp4_from_f32x2<1>(ca, a[2] * la, a[3] * la, 1.0f);
-  unsigned cb = fp4_from_f32x2<0>(0u, b[0] * lb, b[1] * lb, 1.0f);
-  cb = fp4_from_f32x2<1>(cb, b[2] * lb, b[3] * lb, 1.0f);
-  oa = u32x2{nv_bf16_pair<0>(ca, ka), nv_bf16_pair<1>(ca, ka)};
-  ob = u32x2{nv_bf16_pair<0>(cb, kb), nv_bf16_pair<1>(cb, kb)};
 }
 
 // The MX step of one 32-group in the 16x16 layout: scale byte, scale
@@ -566,7 +528,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 template <int FMT>
 __global__ __launch_bounds__(T16_THREADS) __attribute__((amdgpu_waves_per_eu(T16_WAVES_PER_SIMD)))
 void k_rot128_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__ rot,
-                  uint16_t *__restrict__ dst, int64_t n_blk, const float *__restrict__ gp) {
+                  uint16_t *__restrict__ dst, int64_t n_blk) {
+  static_assert(FMT == 0 || FMT == 1, "MX formats");
   constexpr int THREADS = T16_THREADS, TPW = T16_TPW, NR = T16_NR;
   constexpr int RB = 128, NJT = 8, NKB = 4, TB = 16;  // 16-wide j tiles, 32-deep k steps, blocks per tile
   constexpr int TP = TB * 16;                       // 16-byte input pieces per tile
@@ -634,15 +597,6 @@ void k_rot128_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__
   __syncthreads();
 
   u32x4 *T = sT[wave];
-  // NVFP4: the per-tensor constants, and whether g is in the range of the
-  // division-free quotients (see nv_mul)
-  NvTensor nvt{};
-  bool fast = true;
-  if constexpr (FMT == 2) {
-    const float g = *gp;
-    fast = nv_fast(g);
-    nvt = fast ? nv_tensor<true>(g) : nv_tensor<false>(g);
-  }
   for (;;) {
     const int64_t t0 = (unit * WAVES + wave) * TPW;
 #pragma unroll
@@ -671,19 +625,11 @@ void k_rot128_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__
             acc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 __builtin_bit_cast(bf16x8, sA[((2 * gq + hh) * NKB + kb) * 64 + lane]),
                 __builtin_bit_cast(bf16x8, b[kb]), acc[hh], 0, 0, 0);
-        u32x2 oa, ob;
-        if constexpr (FMT == 2) {
-          // NVFP4: run a is a quarter of 16-group 2gq, run b of 2gq+1 (the
-          // same lanes n, n+16, n+32, n+48 hold both)
-          nv16_bf16(acc[0], acc[1], nvt, fast, oa, ob);
-        } else {
-          unsigned sb, ca, cb;
-          float sc;
-          group16_codes<FMT>(acc[0], acc[1], sb, sc, ca, cb);
-          oa = run_bf16<FMT>(ca, sc);
-          ob = run_bf16<FMT>(cb, sc);
-          if (sb == 255u) oa = ob = u32x2{BF16_NAN | (BF16_NAN << 16), BF16_NAN | (BF16_NAN << 16)};
-        }
+        unsigned sb, ca, cb;
+        float sc;
+        group16_codes<FMT>(acc[0], acc[1], sb, sc, ca, cb);
+        u32x2 oa = run_bf16<FMT>(ca, sc), ob = run_bf16<FMT>(cb, sc);
+        if (sb == 255u) oa = ob = u32x2{BF16_NAN | (BF16_NAN << 16), BF16_NAN | (BF16_NAN << 16)};
         // run a: elements 32gq + 4p.. = piece 4gq + p/2, half p%2; run b: 2 pieces on
         ((u32x2 *)T)[2 * slot16(n, 4 * gq + (p >> 1)) + (p & 1)] = oa;
         ((u32x2 *)T)[2 * slot16(n, 4 * gq + 2 + (p >> 1)) + (p & 1)] = ob;
@@ -839,22 +785,19 @@ static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
   return (unsigned)(g < cap ? g : cap);
 }
 
-// QDQ at RB = 128 runs on 16-block tiles (k_rot128_t16), one workgroup per
-// T16_TPW tiles of each of its waves, NVFP4 included: its 16-groups span
-// four lanes there instead of two, so each lane repeats a group's scale
-// steps for twice as many elements, but with the division-free quotients it
-// measured 4% faster than the lane-owned kernel.  Quantize (whose outputs
-// are a quarter of QDQ's) runs on the lane-owned kernel.
+// MX QDQ at RB = 128 runs on 16-block tiles (k_rot128_t16), one workgroup
+// per T16_TPW tiles of each of its waves.  Quantize (whose outputs are a
+// quarter of QDQ's) and NVFP4 run on the lane-owned kernel.
 
 template <int FMT, int OP, int RB>
 static void run_staged(const void *src, const void *rot, int r, void *dst, uint8_t *codes, uint8_t *scales,
                        int64_t n, hipStream_t st, const BlockedScales *bl, const float *gp = nullptr) {
   const int64_t n_blk = n / RB;
-  if constexpr (RB == 128 && OP == OP_QDQ) {
+  if constexpr (RB == 128 && FMT != 2 && OP == OP_QDQ) {
     const int64_t units = ((n_blk + 15) / 16 + (T16_THREADS / 64) * T16_TPW - 1) / ((T16_THREADS / 64) * T16_TPW);
     const unsigned g = (unsigned)(units < ((int64_t)1 << 30) ? units : ((int64_t)1 << 30));
     k_rot128_t16<FMT><<<g, T16_THREADS, 0, st>>>((const uint16_t *)src, (const uint16_t *)rot, (uint16_t *)dst,
-                                                 n_blk, gp);
+                                                 n_blk);
     return;
   } else {
     using Cfg = StagedCfg<RB>;
@@ -918,18 +861,21 @@ static void dispatch_rb(int dtype, const void *src, const void *rot, int r, void
 }
 
 // Which bf16 rotations run on the lane-owned kernels of rotl.hip: r = 128
-// quantize, MX (row-major scales, or blocked scales written by whole units)
-// and NVFP4.  Measured on MI355X against the kernels here, on the
-// 8192 x 57344 layer, same box and run: MX quantize MXFP4 / MXFP8 3% / 2%
-// faster, NVFP4 quantize 5% faster.  QDQ at r = 128, MX and NVFP4, runs on
-// the short-lived 16-block kernel, which measured faster than the lane-owned
-// one; at r <= 64 the lane-owned kernel is slower (the full 128-wide
-// contraction where the 64-element blocks here do a half or less).
-static bool lanes_for(int op, int r) { return r == 128 && op == OP_QUANT; }
+// for MX quantize (row-major scales, or blocked scales written by whole
+// units) and for NVFP4 (QDQ and quantize).  Measured on MI355X against the
+// kernels here, on the 8192 x 57344 layer, same box and run: MX quantize
+// MXFP4 / MXFP8 3% / 2% faster, NVFP4 quantize 5% faster.  NVFP4 QDQ on
+// the 16-block kernel measured 3-4% faster in interleaved A/B, but as
+// bench.py times it (launches back to back, after the unrotated NVFP4 QDQ)
+// 391-400 us against 333 us here.  MX QDQ at r = 128 runs on the 16-block
+// kernel (310 against 349-358 us here); at r <= 64 the lane-owned kernel is
+// slower (the full 128-wide contraction where the 64-element blocks here do
+// a half or less).
+static bool lanes_for(int fmt, int op, int r) { return r == 128 && (op == OP_QUANT || fmt == 2); }
 
 hipError_t launch_nv_rot(int op, const void *src, const void *rot, int r, void *dst, uint8_t *codes,
                          uint8_t *scales, const float *gp, int64_t n, hipStream_t st) {
-  if (lanes_for(op, r)) return launch_rot_lanes(2, op, src, rot, r, dst, codes, scales, n, st, nullptr, gp);
+  if (lanes_for(2, op, r)) return launch_rot_lanes(2, op, src, rot, r, dst, codes, scales, n, st, nullptr, gp);
   const int rb = staged_rb(r, n, nullptr);
   if (op == OP_QDQ) {
     if (rb == 32) run_staged<2, OP_QDQ, 32>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
@@ -945,7 +891,7 @@ hipError_t launch_nv_rot(int op, const void *src, const void *rot, int r, void *
 
 hipError_t launch_rot(int fmt, int op, int dtype, const void *src, const void *rot, int r, void *dst,
                       uint8_t *codes, uint8_t *scales, int64_t n, hipStream_t st, const BlockedScales *bl) {
-  if (dtype == 0 && op != OP_ROTATE && lanes_for(op, r))
+  if (dtype == 0 && op != OP_ROTATE && lanes_for(fmt, op, r))
     return launch_rot_lanes(fmt, op, src, rot, r, dst, codes, scales, n, st, bl);
   if (op == OP_ROTATE) {
     dispatch_rb<0, OP_ROTATE>(dtype, src, rot, r, dst, codes, scales, n, st, nullptr);

@@ -1,8 +1,8 @@
 // Rotated MX and NVFP4 kernels with the rotation matrix held in registers
 // and every lane owning whole 16-byte pieces of the output.  The library
-// runs the quantize forms here (rotation 128); the QDQ forms of the same
-// templates measured 4-12% slower than the 16-block short-lived kernel of
-// rot.hip, which runs them.
+// runs MX quantize and NVFP4 QDQ and quantize here (rotation 128); the MX
+// QDQ forms of the same templates measured 4-12% slower than the 16-block
+// short-lived kernel of rot.hip, which runs them.
 //
 // "[Transform] [Quantization] Add QuTLASS support to vLLM", Online
 // rotations: each r-chunk x of a row becomes y = x . R (y[j] = sum_t x[t]
@@ -50,6 +50,8 @@
 //     of 8 to 64 consecutive tiles per wave and against short-lived
 //     workgroups, quantize 4-7% faster; against 4-wave workgroups, MXFP4
 //     quantize 3-6% faster.
+#include <type_traits>
+
 #include "launch.h"
 #include "mx_device.h"
 
@@ -507,12 +509,15 @@ hipError_t launch_rot_lanes(int fmt, int op, const void *src, const void *rot, i
   const BlockedScales none{0, 0, 0};
   const BlockedScales &b = bl ? *bl : none;
   constexpr int NB = RL_NB;
-  // QDQ at r = 128 runs on the 16-block short-lived kernel (rot.hip), which
-  // measured 4-12% faster; this kernel takes the quantize forms
-  if (op != OP_QUANT) return hipErrorInvalidValue;
+  // MX QDQ at r = 128 runs on the 16-block short-lived kernel (rot.hip),
+  // which measured 4-12% faster; this kernel takes MX quantize and NVFP4
   if (fmt == 2) {
-    rl::launch<2, OP_QUANT, 0, NB, rl_unit<2, OP_QUANT>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
-  } else if (bl == nullptr) {
+    if (op == OP_QDQ) rl::launch<2, OP_QDQ, 0, NB, rl_unit<2, OP_QDQ>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
+    else rl::launch<2, OP_QUANT, 0, NB, rl_unit<2, OP_QUANT>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
+    return hipGetLastError();
+  }
+  if (op != OP_QUANT) return hipErrorInvalidValue;
+  if (bl == nullptr) {
     if (fmt == 0) rl::launch<0, OP_QUANT, 0, NB, rl_unit<0, OP_QUANT>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
     else rl::launch<1, OP_QUANT, 0, NB, rl_unit<1, OP_QUANT>()>(src, rot, r, dst, codes, scales, n, st, b, gp, cap);
   } else {
