@@ -13,7 +13,10 @@ bytes per element: QDQ 2 + 2; quantize 2 + 0.5 + 1/32 (MXFP4) or 2 + 1 + 1/32
 (MXFP8); the rotation matrix (<= 32 KiB) is not counted.
 
 Each launch is bracketed by HIP events on the stream it runs on (the binding
-launches on torch's current stream).  The roofline entry is the launch of
+launches on torch's current stream): one event before the step's first
+launch and one after every launch, so that consecutive launches share the
+event between them (each event record costs the GPU a few microseconds; two
+per launch made the step 1.5% slower).  The roofline entry is the launch of
 the step with the longest average duration: its algorithmic bytes over that
 duration, against 8 TB/s.
 
@@ -397,20 +400,20 @@ def main():
             mx.mx_quantize(fmt, x, rot=R, codes=codes[fmt], scales=scales)
 
     def step(events=None):
+        # events[i] and events[i + 1] bracket launch i
+        if events is not None:
+            events[0].record()
         for i, v in enumerate(var):
-            if events is not None:
-                events[i][0].record()
             launch(*v)
             if events is not None:
-                events[i][1].record()
+                events[i + 1].record()
 
     progress("step: warm-up and timed steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in var]
-          for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(var) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -514,7 +517,7 @@ def main():
     per = []
     step_bytes = 0.0
     for i, (op, fmt, r) in enumerate(var):
-        ms = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        ms = [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
         avg = float(np.mean(ms))
         b = n * bytes_per_element(op, fmt)
         step_bytes += b
