@@ -437,26 +437,25 @@ __attribute__((amdgpu_waves_per_eu(StagedCfg<RB>::resident * THREADS / 256))) vo
 }
 
 // ---------------------------------------------------------------------------
-// RB = 128 on 16-block tiles (4 KiB per wave) with v_mfma_f32_16x16x32_bf16.
+// RB = 64 and 128 on 16-block tiles (2 or 4 KiB per wave) with
+// v_mfma_f32_16x16x32_bf16.
 //
 // Streaming whole 8 KiB tiles per wave (32 blocks, the 32x32 layout above)
 // is slower on this GPU than 4 KiB ones: a persistent copy with the same
 // sweep runs at 5.8 TB/s with 8 KiB per wave and 6.1 TB/s with 4 KiB.  The
 // 16x16x32 MFMA needs only 16 blocks per tile.  Y^T = Reff^T . X^T with
-// m = output j (16 per jt, 8 jt), k = t (32 per kb, 4 kb), n = block:
+// m = output j (16 per jt, RB/16 jt), k = t (32 per kb, RB/32 kb),
+// n = block:
 //   lane l = 16p + n;  B fragment kb: x[block n][t = 32kb + 8p + i];
 //   A fragment (jt, kb): Reff[32kb + 8p + i][16jt + n], i = 0..7;
 //   accumulator jt: y[block n][j = 16jt + 4p + i], i = 0..3.
 // The 32-group g is jt 2g and 2g+1: lane l holds its elements 4p..4p+3
 // ("run a") and 16+4p..16+4p+3 ("run b"), and the group spans lanes n,
 // n+16, n+32, n+48 (two lane swaps reduce the abs-max).  MX formats only.
-// LDS: a tile is 16 blocks x 16 pieces of 16 bytes; piece c of block n sits
-// at slot 16n + (c ^ n), so the fragment reads (16 lanes, one block each,
-// same c) and the coalesced accesses (16 lanes, one block's 16 pieces) are
-// both free of bank conflicts.
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ int slot16(int n, int c) { return 16 * n + (c ^ n); }
+// LDS: a tile is 16 blocks x RB/8 pieces of 16 bytes; piece c of block n
+// sits at slot (RB/8) n + (c ^ (n % (RB/8))), so the fragment reads
+// (16 lanes, one block each, same c) and the coalesced accesses (a block's
+// pieces in consecutive lanes) are both free of bank conflicts.
 
 // Max of v over lanes l, l^16, l^32 and l^48.
 __device__ __forceinline__ unsigned max_across_quarters(unsigned v) {
@@ -506,18 +505,32 @@ __device__ __forceinline__ u32x2 run_bf16(unsigned c, float sc) {
                __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, sc, true))};
 }
 
-// T16_THREADS per workgroup; three fit a CU's LDS (32 KiB of A fragments
-// plus a 4 KiB tile per wave each), so T16_WAVES_PER_SIMD waves share each
-// SIMD: the register budget the compiler schedules for.  Each wave takes
-// T16_TPW consecutive tiles and keeps T16_NR of them in registers ahead of
-// the one it works on.
-constexpr int T16_THREADS = 256, T16_WAVES_PER_SIMD = 3, T16_TPW = 8, T16_NR = 4;
+// Launch shape of the 16-block kernel: threads per workgroup, the waves per
+// SIMD the register budget is compiled for, tiles per wave and tiles kept in
+// registers ahead of the one a wave works on.  RB = 128: three workgroups
+// fit a CU's LDS (32 KiB of A fragments plus a 4 KiB tile per wave each).
+// RB = 64 (2 KiB tiles): one tile per wave, the shortest-lived workgroups,
+// measured fastest on the 8192 x 57344 layer (MXFP4 QDQ at r = 16, 32:
+// 295 and 293 us, against 299-300 with two tiles per wave, 305-321 with
+// four, 313-356 with 8 to 32).
+template <int RB> struct T16Cfg;
+template <> struct T16Cfg<128> {
+  static constexpr int threads = 256, waves_per_simd = 3, tpw = 8, nr = 4;
+};
+template <> struct T16Cfg<64> {
+  static constexpr int threads = 256, waves_per_simd = 4, tpw = 1, nr = 1;
+};
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// MX QDQ (bf16 in and out) with rotation 128 on 16-block tiles.  A short-
-// lived workgroup: R (row-major 128 x 128 bf16) is copied into LDS, the A
+// Slot of piece c of block n in a tile buffer of PPB pieces per block.
+template <int PPB>
+__device__ __forceinline__ int tslot(int n, int c) { return PPB * n + (c ^ (n & (PPB - 1))); }
+
+// MX QDQ (bf16 in and out) with a rotation block of RB = 64 or 128 on
+// 16-block tiles.  A short-lived workgroup: Reff (row-major RB x RB bf16;
+// for r < RB the block-diagonal diag(R, ..., R)) is formed in LDS, the A
 // fragments are formed from it with transposed reads (ds_read_b64_tr_b16:
 // within each 16-lane group, lane i receives element i%4 of the 8 bytes
 // that lanes 4r + i/4 address, r = 0..3, so when lane j addresses row
@@ -525,29 +538,32 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // t0 .. t0+3), and the waves then stream their tiles.  The grid covers the
 // tensor once (up to a cap beyond which workgroups loop), so the hardware
 // dispatcher balances the work across CUs.
-template <int FMT>
-__global__ __launch_bounds__(T16_THREADS) __attribute__((amdgpu_waves_per_eu(T16_WAVES_PER_SIMD)))
-void k_rot128_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__ rot,
-                  uint16_t *__restrict__ dst, int64_t n_blk) {
+template <int FMT, int RB>
+__global__ __launch_bounds__(T16Cfg<RB>::threads) __attribute__((amdgpu_waves_per_eu(T16Cfg<RB>::waves_per_simd)))
+void k_rot_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__ rot, int r,
+               uint16_t *__restrict__ dst, int64_t n_blk) {
   static_assert(FMT == 0 || FMT == 1, "MX formats");
-  constexpr int THREADS = T16_THREADS, TPW = T16_TPW, NR = T16_NR;
-  constexpr int RB = 128, NJT = 8, NKB = 4, TB = 16;  // 16-wide j tiles, 32-deep k steps, blocks per tile
-  constexpr int TP = TB * 16;                       // 16-byte input pieces per tile
+  using Cfg = T16Cfg<RB>;
+  constexpr int THREADS = Cfg::threads, TPW = Cfg::tpw, NR = Cfg::nr;
+  constexpr int NJT = RB / 16, NKB = RB / 32, TB = 16;  // 16-wide j tiles, 32-deep k steps, blocks per tile
+  constexpr int PPB = RB / 8;                       // 16-byte pieces per block
+  constexpr int TP = TB * PPB;                      // 16-byte input pieces per tile
   constexpr int NL = TP / 64;                       // coalesced pieces per lane
   constexpr int WAVES = THREADS / 64;
-  constexpr int RP = RB * RB / 8 / THREADS;         // 16-byte pieces of R per thread
-  static_assert(NKB == WAVES && NJT == 2 * WAVES && RP * THREADS * 8 == RB * RB && NR <= TPW,
-                "each wave forms the fragments of one k step");
+  constexpr int RP = RB * RB / 8 / THREADS;         // 16-byte pieces of Reff per thread
+  constexpr int JPW = NJT * NKB / WAVES;            // A fragments (j tiles) a wave forms
+  static_assert(WAVES % NKB == 0 && JPW * WAVES == NJT * NKB && RP * THREADS * 8 == RB * RB && NR <= TPW,
+                "each wave forms the fragments of one k step and a whole share of the j tiles");
   __shared__ u32x4 sA[NJT * NKB * 64];
   __shared__ u32x4 sT[WAVES][TP];
-  static_assert(sizeof(sA) == RB * RB * 2, "R is staged in the fragment buffer");
+  static_assert(sizeof(sA) == RB * RB * 2, "Reff is staged in the fragment buffer");
 
   const int lane = threadIdx.x & 63, p = lane >> 4, n = lane & 15, wave = threadIdx.x >> 6;
   const int64_t n_elem = n_blk * RB;
   const int64_t n_tiles = (n_blk + TB - 1) / TB;
   const int64_t n_units = (n_tiles + WAVES * TPW - 1) / (WAVES * TPW);
 
-  // coalesced loads of one tile: lane piece 64q + lane (block (64q+lane)/16)
+  // coalesced loads of one tile: lane piece 64q + lane (block (64q+lane)/PPB)
   auto load_tile = [&](int64_t tile, u32x4 *v) {
     const int64_t e_tile = tile * TB * RB;
     const u32x4 *gs = (const u32x4 *)(src + e_tile) + lane;
@@ -562,13 +578,22 @@ void k_rot128_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__
     }
   };
 
-  // R and the first NR tiles of this wave, all loads in flight at once
+  // Reff and the first NR tiles of this wave, all loads in flight at once.
+  // Piece x of Reff is row x / PPB, columns 8 (x % PPB) .. +7: inside the
+  // diagonal block of its row it is piece (t % r) r/8 + (j % r)/8 of R,
+  // elsewhere zero (r is a multiple of 16, so no piece straddles a block).
   int64_t unit = blockIdx.x;
   u32x4 v[NR][NL];
   {
     u32x4 rv[RP];
 #pragma unroll
-    for (int k = 0; k < RP; ++k) rv[k] = ((const u32x4 *)rot)[threadIdx.x + k * THREADS];
+    for (int k = 0; k < RP; ++k) {
+      const int x = threadIdx.x + k * THREADS, t = x / PPB, j = 8 * (x % PPB);
+      if (RB == 128 || r == RB)
+        rv[k] = ((const u32x4 *)rot)[x];
+      else
+        rv[k] = t / r == j / r ? ((const u32x4 *)rot)[(t % r) * (r / 8) + (j % r) / 8] : u32x4{0u, 0u, 0u, 0u};
+    }
     const int64_t t0 = (unit * WAVES + wave) * TPW;
 #pragma unroll
     for (int t = 0; t < NR; ++t)
@@ -579,20 +604,22 @@ void k_rot128_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__
   __syncthreads();
   {
     // A fragment (jt, kb) of lane 16p + n: Reff[32kb + 8p + i][16jt + n],
-    // i = 0..7 (Reff = R at r = 128).  Wave w forms those of kb = w.
+    // i = 0..7.  Wave w forms those of kb = w % NKB, jt = j0 .. j0+JPW-1.
     const uint16_t *Rs = (const uint16_t *)sA;
-    const int row = 32 * wave + 8 * p + (n >> 2), col = 4 * (n & 3);
-    u32x4 fa[NJT];
+    const int kbw = wave % NKB, j0 = (wave / NKB) * JPW;
+    const int row = 32 * kbw + 8 * p + (n >> 2), col = 4 * (n & 3);
+    u32x4 fa[JPW];
 #pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) {
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Rs + row * RB + 16 * jt + col));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Rs + (row + 4) * RB + 16 * jt + col));
+    for (int j = 0; j < JPW; ++j) {
+      const int c0 = 16 * (j0 + j) + col;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Rs + row * RB + c0));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Rs + (row + 4) * RB + c0));
       const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
-      fa[jt] = u32x4{a[0], a[1], b[0], b[1]};
+      fa[j] = u32x4{a[0], a[1], b[0], b[1]};
     }
     __syncthreads();
 #pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) sA[(jt * NKB + wave) * 64 + lane] = fa[jt];
+    for (int j = 0; j < JPW; ++j) sA[((j0 + j) * NKB + kbw) * 64 + lane] = fa[j];
   }
   __syncthreads();
 
@@ -605,14 +632,14 @@ void k_rot128_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__
       if (tile >= n_tiles) break;
       const int64_t e_tile = tile * TB * RB;
       const bool full = e_tile + (int64_t)TP * 8 <= n_elem;
-      // 1. the tile into LDS (piece P = 64q + lane is block P/16, piece P%16)
+      // 1. the tile into LDS (piece P = 64q + lane is block P/PPB, piece P%PPB)
 #pragma unroll
-      for (int q = 0; q < NL; ++q) T[slot16(4 * q + p, n)] = v[t % NR][q];
+      for (int q = 0; q < NL; ++q) T[tslot<PPB>((64 * q + lane) / PPB, lane % PPB)] = v[t % NR][q];
       wave_lds_sync();
       // 2. B fragments: block n, pieces 4kb + p
       u32x4 b[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) b[kb] = T[slot16(n, 4 * kb + p)];
+      for (int kb = 0; kb < NKB; ++kb) b[kb] = T[tslot<PPB>(n, 4 * kb + p)];
       wave_lds_sync();
       // 3. rotate and QDQ, one 32-group (jt 2g, 2g+1) at a time
 #pragma unroll
@@ -631,15 +658,15 @@ void k_rot128_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__
         u32x2 oa = run_bf16<FMT>(ca, sc), ob = run_bf16<FMT>(cb, sc);
         if (sb == 255u) oa = ob = u32x2{BF16_NAN | (BF16_NAN << 16), BF16_NAN | (BF16_NAN << 16)};
         // run a: elements 32gq + 4p.. = piece 4gq + p/2, half p%2; run b: 2 pieces on
-        ((u32x2 *)T)[2 * slot16(n, 4 * gq + (p >> 1)) + (p & 1)] = oa;
-        ((u32x2 *)T)[2 * slot16(n, 4 * gq + 2 + (p >> 1)) + (p & 1)] = ob;
+        ((u32x2 *)T)[2 * tslot<PPB>(n, 4 * gq + (p >> 1)) + (p & 1)] = oa;
+        ((u32x2 *)T)[2 * tslot<PPB>(n, 4 * gq + 2 + (p >> 1)) + (p & 1)] = ob;
       }
       wave_lds_sync();
       // 4. coalesced stores of the tile's outputs
       u32x4 *gd = (u32x4 *)(dst + e_tile) + lane;
       u32x4 o[NL];
 #pragma unroll
-      for (int q = 0; q < NL; ++q) o[q] = T[slot16(4 * q + p, n)];
+      for (int q = 0; q < NL; ++q) o[q] = T[tslot<PPB>((64 * q + lane) / PPB, lane % PPB)];
       if (full) {
 #pragma unroll
         for (int q = 0; q < NL; ++q) __builtin_nontemporal_store(o[q], gd + q * 64);
@@ -785,21 +812,32 @@ static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
   return (unsigned)(g < cap ? g : cap);
 }
 
-// MX QDQ at RB = 128 runs on 16-block tiles (k_rot128_t16), one workgroup
-// per T16_TPW tiles of each of its waves.  Quantize (whose outputs are a
-// quarter of QDQ's) and NVFP4 run on the lane-owned kernel.
+// MX QDQ runs on 16-block tiles (k_rot_t16, one workgroup per tpw tiles of
+// each of its waves) at RB = 128, and at RB = 64 when r < 64: there each
+// workgroup forms Reff from a half or a quarter of R's bytes (the rest are
+// the block-diagonal's zeros).  Measured on the 8192 x 57344 layer, bench-
+// style blocks of 20 launches: r = 16 307 -> 295 us, r = 32 303 -> 293 us
+// against the 32-block tiles here, but r = 64, whose workgroups each read
+// all of R, 300 -> 302-304 us, so r = 64 stays on the 32-block tiles.
+// Quantize (whose outputs are a quarter of QDQ's) and NVFP4 at RB = 128 run
+// on the lane-owned kernel, and at RB = 32 and 64 on the 32-block tiles.
 
 template <int FMT, int OP, int RB>
 static void run_staged(const void *src, const void *rot, int r, void *dst, uint8_t *codes, uint8_t *scales,
                        int64_t n, hipStream_t st, const BlockedScales *bl, const float *gp = nullptr) {
   const int64_t n_blk = n / RB;
-  if constexpr (RB == 128 && FMT != 2 && OP == OP_QDQ) {
-    const int64_t units = ((n_blk + 15) / 16 + (T16_THREADS / 64) * T16_TPW - 1) / ((T16_THREADS / 64) * T16_TPW);
-    const unsigned g = (unsigned)(units < ((int64_t)1 << 30) ? units : ((int64_t)1 << 30));
-    k_rot128_t16<FMT><<<g, T16_THREADS, 0, st>>>((const uint16_t *)src, (const uint16_t *)rot, (uint16_t *)dst,
-                                                 n_blk);
-    return;
-  } else {
+  if constexpr ((RB == 128 || RB == 64) && FMT != 2 && OP == OP_QDQ) {
+    if (RB == 128 || r < 64) {
+      using Cfg = T16Cfg<RB>;
+      constexpr int64_t per_unit = (Cfg::threads / 64) * Cfg::tpw;  // tiles per workgroup
+      const int64_t units = ((n_blk + 15) / 16 + per_unit - 1) / per_unit;
+      const unsigned g = (unsigned)(units < ((int64_t)1 << 30) ? units : ((int64_t)1 << 30));
+      k_rot_t16<FMT, RB><<<g, Cfg::threads, 0, st>>>((const uint16_t *)src, (const uint16_t *)rot, r,
+                                                    (uint16_t *)dst, n_blk);
+      return;
+    }
+  }
+  if constexpr (!(RB == 128 && FMT != 2 && OP == OP_QDQ)) {
     using Cfg = StagedCfg<RB>;
     const int64_t tiles = (n_blk + 31) / 32;
     int per_cu = OP == OP_QDQ ? Cfg::per_cu_qdq : Cfg::per_cu;

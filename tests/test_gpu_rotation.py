@@ -140,14 +140,28 @@ def test_rot128_qdq_work_unit_edges(mx, fmt, shape):
     _qdq_band(mx, fmt, x, W.hadamard_rotation(128), 128)
 
 
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
+@pytest.mark.parametrize("r", [16, 32])
+def test_rot_le32_qdq_work_unit_edges(mx, fmt, r):
+    """QDQ with r = 16 or 32 runs on 64-element blocks in workgroups of 4
+    tiles of 16 blocks: one block, a tile less one block, one tile, a tile
+    plus one block, a workgroup less one block, one workgroup, a workgroup
+    plus one block, and longer rows with a partial last tile, all within the
+    band of the oracle."""
+    R = W.hadamard_rotation(r)
+    for shape in [(1, 64), (15, 64), (16, 64), (17, 64), (63, 64), (64, 64), (65, 64), (3, 4160), (31, 2112)]:
+        x = W.random_bf16(shape, seed=shape[0] * 13 + shape[1] + r + fmt)
+        _qdq_band(mx, fmt, x, R, r)
+
+
 @pytest.mark.parametrize("shape", [(1, 128), (16, 2048), (1931, 2176)], ids=lambda s: f"{s[0]}x{s[1]}")
 def test_rot128_lane_kernel_grid_edges(mx, shape):
-    """Quantize (MX and NVFP4) at r = 128 runs on a persistent grid of one
-    wave per workgroup, 8 per CU, whose waves take interleaved 16-block
-    tiles, and NVFP4 QDQ on short-lived workgroups of 8 tiles per wave: one
-    partial tile, exactly 16 tiles, and 2052 tiles (the last one partial) so
-    that the first waves take a second tile.  MX quantize and NVFP4 QDQ and
-    quantize of every row within the band of the oracle."""
+    """Quantize (MX and NVFP4) and NVFP4 QDQ at r = 128 run on a persistent
+    grid of one wave per workgroup, 8 per CU, whose waves take interleaved
+    16-block tiles: one partial tile, exactly 16 tiles, and 2052 tiles (the
+    last one partial) so that the first waves take a second tile.  MX
+    quantize and NVFP4 QDQ and quantize of every row within the band of the
+    oracle."""
     import torch
     from _bandcheck import check_nv
     x = W.random_bf16(shape, seed=shape[0] + 17)
