@@ -452,10 +452,10 @@ __attribute__((amdgpu_waves_per_eu(StagedCfg<RB>::resident * THREADS / 256))) vo
 // The 32-group g is jt 2g and 2g+1: lane l holds its elements 4p..4p+3
 // ("run a") and 16+4p..16+4p+3 ("run b"), and the group spans lanes n,
 // n+16, n+32, n+48 (two lane swaps reduce the abs-max).  MX formats only.
-// LDS: a tile is 16 blocks x RB/8 pieces of 16 bytes; piece c of block n
-// sits at slot (RB/8) n + (c ^ (n % (RB/8))), so the fragment reads
-// (16 lanes, one block each, same c) and the coalesced accesses (a block's
-// pieces in consecutive lanes) are both free of bank conflicts.
+// LDS: a tile is 16 blocks x RB/8 pieces of 16 bytes, XOR-swizzled (tslot)
+// so that the fragment reads (16 lanes, one block each, same piece) and the
+// coalesced accesses (a block's pieces in consecutive lanes) are both free
+// of bank conflicts.
 
 // Max of v over lanes l, l^16, l^32 and l^48.
 __device__ __forceinline__ unsigned max_across_quarters(unsigned v) {
@@ -524,9 +524,12 @@ template <> struct T16Cfg<64> {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// Slot of piece c of block n in a tile buffer of PPB pieces per block.
+// Slot of piece c of block n in a tile buffer of PPB (16 or 8) pieces per
+// block: the XOR key n / (16 / PPB) makes the 16 blocks of a fragment read
+// (same c) and a block's PPB pieces in consecutive lanes fall on distinct
+// 16-byte bank groups of a 256-byte LDS row.
 template <int PPB>
-__device__ __forceinline__ int tslot(int n, int c) { return PPB * n + (c ^ (n & (PPB - 1))); }
+__device__ __forceinline__ int tslot(int n, int c) { return PPB * n + (c ^ ((n / (16 / PPB)) & (PPB - 1))); }
 
 // MX QDQ (bf16 in and out) with a rotation block of RB = 64 or 128 on
 // 16-block tiles.  A short-lived workgroup: Reff (row-major RB x RB bf16;
@@ -586,13 +589,15 @@ void k_rot_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__ ro
   u32x4 v[NR][NL];
   {
     u32x4 rv[RP];
+    const int rs = __builtin_ctz(r);  // r is a power of two
 #pragma unroll
     for (int k = 0; k < RP; ++k) {
       const int x = threadIdx.x + k * THREADS, t = x / PPB, j = 8 * (x % PPB);
       if (RB == 128 || r == RB)
         rv[k] = ((const u32x4 *)rot)[x];
       else
-        rv[k] = t / r == j / r ? ((const u32x4 *)rot)[(t % r) * (r / 8) + (j % r) / 8] : u32x4{0u, 0u, 0u, 0u};
+        rv[k] = (t >> rs) == (j >> rs) ? ((const u32x4 *)rot)[((t & (r - 1)) << (rs - 3)) + ((j & (r - 1)) >> 3)]
+                                       : u32x4{0u, 0u, 0u, 0u};
     }
     const int64_t t0 = (unit * WAVES + wave) * TPW;
 #pragma unroll
