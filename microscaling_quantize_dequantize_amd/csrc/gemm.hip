@@ -75,24 +75,13 @@ using IC = std::integral_constant<int, N>;
 // GEMM-shaped slices (64 KB per CU): loads alone take 0.78 us per slice and
 // MFMAs alone 1.05 us; a burst of each wave's 16 loads ahead of its 64 MFMAs
 // takes 1.5 us, the same loads issued by other waves 1.15 us.
-#ifndef MXG_JA4
-#define MXG_JA4 4
-#endif
-#ifndef MXG_JB4
-#define MXG_JB4 4
-#endif
-#ifndef MXG_JS04
-#define MXG_JS04 8
-#endif
-#ifndef MXG_JA8
-#define MXG_JA8 8
-#endif
-#ifndef MXG_JB8
-#define MXG_JB8 8
-#endif
-#ifndef MXG_SPLIT4
-#define MXG_SPLIT4 1
-#endif
+// A slice's load jobs issued between its two barriers (JA), after the
+// publishing barrier (JB) and, for E2M1, during the next slice's first
+// k-step (JS0); the rest go out in its second.  E2M1 also takes two
+// barriers per slice (one measured 3-4% slower once the loads were paced).
+constexpr int GEMM_JA4 = 4, GEMM_JB4 = 4, GEMM_JS04 = 8;  // E2M1
+constexpr int GEMM_JA8 = 8, GEMM_JB8 = 8;                  // E4M3
+constexpr bool GEMM_SPLIT4 = true;
 
 
 // the number of n events, spread evenly over m slots, that fall in slot k
@@ -167,14 +156,14 @@ __global__ __launch_bounds__(GT) void k_mx_gemm(const uint8_t *__restrict__ A, c
   // last fragments have been read: E4M3 2.12 -> 1.95 ms (row-major scales)
   // and 1.79 -> 1.69 ms (blocked) when the loads went out in one burst; with
   // paced loads, E2M1 gains 3-4% over one barrier.
-  constexpr bool SPLIT = FMT == 1 || MXG_SPLIT4;
+  constexpr bool SPLIT = FMT == 1 || GEMM_SPLIT4;
   // a slice's load jobs: the code loads, then the scale loads that travel
   // with it; JA are issued between the two barriers (SPLIT), JB after the
   // publishing barrier, JS0 and JS1 during the next slice's k-steps 0 and 1
   constexpr int NJ = 2 * DMA_W + (SL == 1 || SDMA ? 2 : 0);
-  constexpr int JA0 = !SPLIT ? 0 : FMT == 0 ? MXG_JA4 : MXG_JA8, JA = JA0 < NJ ? JA0 : NJ;
-  constexpr int JB0 = FMT == 0 ? MXG_JB4 : MXG_JB8, JB = JB0 < NJ - JA ? JB0 : NJ - JA;
-  constexpr int JS0 = FMT == 0 ? (NJ - JA - JB < MXG_JS04 ? NJ - JA - JB : MXG_JS04) : NJ - JA - JB;
+  constexpr int JA0 = !SPLIT ? 0 : FMT == 0 ? GEMM_JA4 : GEMM_JA8, JA = JA0 < NJ ? JA0 : NJ;
+  constexpr int JB0 = FMT == 0 ? GEMM_JB4 : GEMM_JB8, JB = JB0 < NJ - JA ? JB0 : NJ - JA;
+  constexpr int JS0 = FMT == 0 ? (NJ - JA - JB < GEMM_JS04 ? NJ - JA - JB : GEMM_JS04) : NJ - JA - JB;
   constexpr int JS1 = NJ - JA - JB - JS0;
   static_assert(JA >= 0 && JB >= 0 && JS0 >= 0 && JS1 >= 0 && (NS == 4 || JS1 == 0), "job schedule");
   // register scale loads issued with the slice after next (SREG)

@@ -59,10 +59,7 @@ namespace mx {
 
 namespace rl {
 
-#ifndef RL_THREADS
-#define RL_THREADS 64
-#endif
-constexpr int THREADS = RL_THREADS;          // 1 or 4 waves per workgroup
+constexpr int THREADS = 64;                  // one wave per workgroup (the code also takes 4)
 constexpr int WAVES = THREADS / 64;
 constexpr int RB = 128;                      // elements per rotation block
 constexpr int TB = 16;                       // blocks per tile
@@ -70,9 +67,7 @@ constexpr int TILE_ELEMS = TB * RB;          // 2048
 constexpr int TILE_BYTES = TILE_ELEMS * 2;   // 4 KiB of bf16
 constexpr int RSRC_FLAGS = 0x00020000;       // raw 32-bit buffer
 constexpr unsigned OOB_OFFSET = 0x80000000u;  // a buffer offset past every record
-#ifndef RL_AUX
-#define RL_AUX 2                             // cache policy of the tile loads: non-temporal
-#endif
+constexpr int AUX_NT = 2;                    // cache policy of the tile loads and code stores: non-temporal
 
 template <int NB> struct Lds {
   static constexpr int ring = WAVES * NB * TILE_BYTES;
@@ -195,10 +190,10 @@ __device__ __forceinline__ void unit_tile_epilogue(const f32x4 (&acc)[8], int64_
     opaque_offset(off);
     if (FMT == 0) {
       if (sb == 255u) c.x = 0u;
-      __builtin_amdgcn_raw_buffer_store_b32(c.x, rc, off, 0, RL_AUX);
+      __builtin_amdgcn_raw_buffer_store_b32(c.x, rc, off, 0, AUX_NT);
     } else {
       if (sb == 255u) c = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
-      __builtin_amdgcn_raw_buffer_store_b64(c, rc, off, 0, RL_AUX);
+      __builtin_amdgcn_raw_buffer_store_b64(c, rc, off, 0, AUX_NT);
     }
     // group n/4 of this block at unit position: word 32 h + row, byte g8 / 2,
     // g8 = 4 (p % 2) + n / 4 the group within the unit, h = g8 % 2
@@ -285,7 +280,7 @@ __device__ __forceinline__ void rot_lanes_tiles(const uint16_t *__restrict__ src
     for (int q = 0; q < 4; ++q) {
       unsigned off = drop ? OOB_OFFSET : voff[q];
       opaque_offset(off);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, RL_LDS(buf + 1024 * q), 16, off, 0, 0, RL_AUX);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, RL_LDS(buf + 1024 * q), 16, off, 0, 0, AUX_NT);
     }
   };
   // A fragment reads: lane (p, m = n) takes block beta(m), piece 4 kb + p
@@ -495,12 +490,7 @@ static void launch(const void *src, const void *rot, int r, void *dst, uint8_t *
 // in one process: 2-tile units 4% faster than 1 for MXFP8 quantize and
 // NVFP4 QDQ, 7% slower for MXFP4 and NVFP4 quantize; 4-tile units slower
 // still; a ring of 4 tiles as fast as 5.
-#ifndef RL_NB
-#define RL_NB 4
-#endif
-#ifndef RL_PER_CU
-#define RL_PER_CU 8
-#endif
+constexpr int RL_NB = 4, RL_PER_CU = 8;
 template <int FMT, int OP> constexpr int rl_unit() { return (FMT == 1 && OP == OP_QUANT) || (FMT == 2 && OP == OP_QDQ) ? 2 : 1; }
 
 hipError_t launch_rot_lanes(int fmt, int op, const void *src, const void *rot, int r, void *dst, uint8_t *codes,
