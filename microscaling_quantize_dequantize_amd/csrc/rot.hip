@@ -200,13 +200,11 @@ __device__ __forceinline__ void group_fp8_bytes(const unsigned c[4], unsigned sb
 // (16 waves) for RB = 64 run 2-3% faster than the 32 and 24 waves that fit
 // otherwise.  For RB = 64 a grid of 32 per CU (about 3.5 tiles per wave) is
 // fastest for quantize and 48 (about 2.3) for QDQ (per_cu_qdq; 1-2% faster
-// than 32 for QDQ, 3-4% slower for blocked-scale quantize); for RB = 128
-// (quantize and NVFP4) a persistent grid of exactly the resident count (a
-// grid that is not a multiple of it leaves a partial last round).
+// than 32 for QDQ, 3-4% slower for blocked-scale quantize).  (RB = 128
+// runs on k_rot_t16 and the lane-owned kernels.)
 template <int RB> struct StagedCfg;
 template <> struct StagedCfg<32> { static constexpr int threads = 1024, per_cu = 8, per_cu_qdq = 8, resident = 1; };
 template <> struct StagedCfg<64> { static constexpr int threads = 512, per_cu = 32, per_cu_qdq = 48, resident = 2; };
-template <> struct StagedCfg<128> { static constexpr int threads = 256, per_cu = 2, per_cu_qdq = 2, resident = 2; };
 
 constexpr int LDS_PER_CU = 160 * 1024;
 
@@ -895,7 +893,8 @@ static void dispatch_rb(int dtype, const void *src, const void *rot, int r, void
   if (dtype == 0 && OP != OP_ROTATE) {
     if (rb == 32) run_staged<FMT, OP, 32>(src, rot, r, dst, codes, scales, n, st, bl);
     else if (rb == 64) run_staged<FMT, OP, 64>(src, rot, r, dst, codes, scales, n, st, bl);
-    else run_staged<FMT, OP, 128>(src, rot, r, dst, codes, scales, n, st, bl);
+    else if constexpr (OP == OP_QDQ) run_staged<FMT, OP, 128>(src, rot, r, dst, codes, scales, n, st, bl);
+    else (void)launch_rot_lanes(FMT, OP, src, rot, r, dst, codes, scales, n, st, bl);  // (launch_rot sends it there)
   } else if (OP != OP_QUANT) {
     if (rb == 32) run_direct<FMT, OP, 32>(dtype, src, rot, r, dst, n, st);
     else if (rb == 64) run_direct<FMT, OP, 64>(dtype, src, rot, r, dst, n, st);
@@ -919,15 +918,13 @@ static bool lanes_for(int fmt, int op, int r) { return r == 128 && (op == OP_QUA
 hipError_t launch_nv_rot(int op, const void *src, const void *rot, int r, void *dst, uint8_t *codes,
                          uint8_t *scales, const float *gp, int64_t n, hipStream_t st) {
   if (lanes_for(2, op, r)) return launch_rot_lanes(2, op, src, rot, r, dst, codes, scales, n, st, nullptr, gp);
-  const int rb = staged_rb(r, n, nullptr);
+  const int rb = staged_rb(r, n, nullptr);  // 32 or 64: r = 128 runs on the lane-owned kernel
   if (op == OP_QDQ) {
     if (rb == 32) run_staged<2, OP_QDQ, 32>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
-    else if (rb == 64) run_staged<2, OP_QDQ, 64>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
-    else run_staged<2, OP_QDQ, 128>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
+    else run_staged<2, OP_QDQ, 64>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
   } else {
     if (rb == 32) run_staged<2, OP_QUANT, 32>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
-    else if (rb == 64) run_staged<2, OP_QUANT, 64>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
-    else run_staged<2, OP_QUANT, 128>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
+    else run_staged<2, OP_QUANT, 64>(src, rot, r, dst, codes, scales, n, st, nullptr, gp);
   }
   return hipGetLastError();
 }
