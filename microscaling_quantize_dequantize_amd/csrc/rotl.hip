@@ -1,8 +1,8 @@
 // Rotated MX and NVFP4 kernels with the rotation matrix held in registers
 // and every lane owning whole 16-byte pieces of the output.  The library
-// runs MX quantize and NVFP4 QDQ and quantize here (rotation 128); the MX
-// QDQ forms of the same templates measured 4-12% slower than the 16-block
-// short-lived kernel of rot.hip, which runs them.
+// runs MX quantize and NVFP4 QDQ and quantize here (rotation 128); MX QDQ,
+// which measured 4-12% slower here, runs on the 16-block short-lived kernel
+// of rot.hip.
 //
 // "[Transform] [Quantization] Add QuTLASS support to vLLM", Online
 // rotations: each r-chunk x of a row becomes y = x . R (y[j] = sum_t x[t]
@@ -231,6 +231,7 @@ __device__ __forceinline__ void rot_lanes_tiles(const uint16_t *__restrict__ src
                                                 uint8_t *unit_bytes, int lane, int64_t wave_id, int64_t n_waves) {
   const int p = lane >> 4, n = lane & 15;
   static_assert(SL != 2 || (UNIT == 4 && OP == OP_QUANT && FMT != 2), "unit tiles: MX quantize, 4 per unit");
+  static_assert(FMT == 2 || OP == OP_QUANT, "MX QDQ runs on k_rot_t16");
   const int64_t K = SL == 2 ? bl.groups * 32 : 0;
   const int64_t col_pairs = SL == 2 ? bl.gblocks : 0;
   const int64_t n_tiles = SL == 2 ? 4 * ((bl.rows + 31) / 32) * col_pairs : (n_elem + TILE_ELEMS - 1) / TILE_ELEMS;
@@ -356,34 +357,25 @@ __device__ __forceinline__ void rot_lanes_tiles(const uint16_t *__restrict__ src
           float sc;
           u32x2 c;
           piece_codes<FMT>(v, sb, sc, c);
-          if (OP == OP_QDQ) {
-            u32x4 o = FMT == 0 ? bf16x8_from_fp4(c.x, sc) : bf16x8_from_fp8(c, sc);
-            if (sb == 255u) {
-              const unsigned nn = BF16_NAN | (BF16_NAN << 16);
-              o = u32x4{nn, nn, nn, nn};
-            }
-            if (ok) __builtin_nontemporal_store(o, (u32x4 *)(dst + e));
+          if (FMT == 0) {
+            if (sb == 255u) c.x = 0u;
+            if (ok) __builtin_nontemporal_store(c.x, (unsigned *)(codes + e / 2));
           } else {
-            if (FMT == 0) {
-              if (sb == 255u) c.x = 0u;
-              if (ok) __builtin_nontemporal_store(c.x, (unsigned *)(codes + e / 2));
-            } else {
-              if (sb == 255u) c = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
-              if (ok) __builtin_nontemporal_store(c, (u32x2 *)(codes + e));
+            if (sb == 255u) c = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
+            if (ok) __builtin_nontemporal_store(c, (u32x2 *)(codes + e));
+          }
+          if (SL == 1) {
+            if ((lane & 3) == 0 && ok) {
+              const int64_t gf = e >> 5, row = gf / bl.groups;
+              scales[blocked_offset(row, gf - row * bl.groups, bl.gblocks)] = (uint8_t)sb;
             }
-            if (SL == 1) {
-              if ((lane & 3) == 0 && ok) {
-                const int64_t gf = e >> 5, row = gf / bl.groups;
-                scales[blocked_offset(row, gf - row * bl.groups, bl.gblocks)] = (uint8_t)sb;
-              }
-            } else {
-              // lanes 16p .. 16p+15 hold the 4 groups of block 4i + p: after
-              // two row rotations every lane of the row holds their 4 bytes
-              unsigned w = sb << (8 * ((lane >> 2) & 3));
-              w |= dpp<DPP_ROW_ROR4>(w);
-              w |= dpp<DPP_ROW_ROR8>(w);
-              sbw[i] = w;
-            }
+          } else {
+            // lanes 16p .. 16p+15 hold the 4 groups of block 4i + p: after
+            // two row rotations every lane of the row holds their 4 bytes
+            unsigned w = sb << (8 * ((lane >> 2) & 3));
+            w |= dpp<DPP_ROW_ROR4>(w);
+            w |= dpp<DPP_ROW_ROR8>(w);
+            sbw[i] = w;
           }
         }
       }
