@@ -507,13 +507,16 @@ __device__ __forceinline__ u32x2 run_bf16(unsigned c, float sc) {
 // SIMD the register budget is compiled for, tiles per wave and tiles kept in
 // registers ahead of the one a wave works on.  RB = 128: three workgroups
 // fit a CU's LDS (32 KiB of A fragments plus a 4 KiB tile per wave each).
+// RB = 128: four tiles per wave, three of them in registers ahead (bench-
+// style blocks on the 8192 x 57344 layer: 303-306 us against 309-313 with
+// 8 and 4, 313-327 with 2, 3, 5, 6 or 12 tiles per wave).
 // RB = 64 (2 KiB tiles): one tile per wave, the shortest-lived workgroups,
 // measured fastest on the 8192 x 57344 layer (MXFP4 QDQ at r = 16, 32:
 // 295 and 293 us, against 299-300 with two tiles per wave, 305-321 with
 // four, 313-356 with 8 to 32).
 template <int RB> struct T16Cfg;
 template <> struct T16Cfg<128> {
-  static constexpr int threads = 256, waves_per_simd = 3, tpw = 8, nr = 4;
+  static constexpr int threads = 256, waves_per_simd = 3, tpw = 4, nr = 3;
 };
 template <> struct T16Cfg<64> {
   static constexpr int threads = 256, waves_per_simd = 4, tpw = 1, nr = 1;

@@ -129,13 +129,14 @@ def test_hadamard_small_shapes(mx, fmt, r):
 
 
 @pytest.mark.parametrize("fmt", [E2M1, E4M3])
-@pytest.mark.parametrize("shape", [(511, 128), (512, 128), (513, 128), (31, 4224), (16, 8192), (3, 22016)],
+@pytest.mark.parametrize("shape", [(255, 128), (256, 128), (257, 128), (511, 128), (512, 128), (513, 128),
+                                   (31, 4224), (16, 8192), (3, 22016)],
                          ids=lambda s: f"{s[0]}x{s[1]}")
 def test_rot128_qdq_work_unit_edges(mx, fmt, shape):
-    """QDQ with r = 128 runs in work units of 32 tiles of 16 blocks (512
-    rotation blocks): tensors of a unit less one block, one unit, a unit
-    plus one block, one block short of two units, two units, and a partial
-    last tile, all within the band of the oracle."""
+    """QDQ with r = 128 runs in workgroups of 16 tiles of 16 blocks (256
+    rotation blocks): tensors of a workgroup less one block, one, one plus a
+    block, two less one block, two, two plus a block, and partial last
+    tiles, all within the band of the oracle."""
     x = W.random_bf16(shape, seed=shape[0] * 7 + fmt)
     _qdq_band(mx, fmt, x, W.hadamard_rotation(128), 128)
 
