@@ -532,6 +532,13 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 template <int PPB>
 __device__ __forceinline__ int tslot(int n, int c) { return PPB * n + (c ^ ((n / (16 / PPB)) & (PPB - 1))); }
 
+// Slot of piece c of row t of Reff staged in LDS (PPB pieces per row): the
+// key 2 (t % 4) puts the two pieces that a transposed fragment read takes
+// from each of four consecutive rows into eight different 16-byte bank
+// groups (unswizzled, rows 256 or 128 bytes apart share their banks).
+template <int PPB>
+__device__ __forceinline__ int rslot(int t, int c) { return PPB * t + (c ^ (2 * (t & 3))); }
+
 // MX QDQ (bf16 in and out) with a rotation block of RB = 64 or 128 on
 // 16-block tiles.  A short-lived workgroup: Reff (row-major RB x RB bf16;
 // for r < RB the block-diagonal diag(R, ..., R)) is formed in LDS, the A
@@ -605,19 +612,24 @@ void k_rot_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__ ro
     for (int t = 0; t < NR; ++t)
       if (t0 + t < n_tiles) load_tile(t0 + t, v[t]);
 #pragma unroll
-    for (int k = 0; k < RP; ++k) sA[threadIdx.x + k * THREADS] = rv[k];
+    for (int k = 0; k < RP; ++k) {
+      const int x = threadIdx.x + k * THREADS;
+      sA[rslot<PPB>(x / PPB, x % PPB)] = rv[k];
+    }
   }
   __syncthreads();
   {
     // A fragment (jt, kb) of lane 16p + n: Reff[32kb + 8p + i][16jt + n],
     // i = 0..7.  Wave w forms those of kb = w % NKB, jt = j0 .. j0+JPW-1.
+    // Lane n reads 8 bytes at column 16jt + 4 (n % 4): piece 2jt + (n % 4) / 2,
+    // half n % 2, of rows `row` and `row` + 4 (the same key).
     const uint16_t *Rs = (const uint16_t *)sA;
     const int kbw = wave % NKB, j0 = (wave / NKB) * JPW;
-    const int row = 32 * kbw + 8 * p + (n >> 2), col = 4 * (n & 3);
+    const int row = 32 * kbw + 8 * p + (n >> 2);
     u32x4 fa[JPW];
 #pragma unroll
     for (int j = 0; j < JPW; ++j) {
-      const int c0 = 16 * (j0 + j) + col;
+      const int c0 = 8 * (rslot<PPB>(row, 2 * (j0 + j) + ((n & 3) >> 1)) - PPB * row) + 4 * (n & 1);
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Rs + row * RB + c0));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Rs + (row + 4) * RB + c0));
       const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
