@@ -701,7 +701,6 @@ void k_rot_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__ ro
     unit += gridDim.x;
     if (unit >= n_units) break;
     const int64_t t1 = (unit * WAVES + wave) * TPW;
-#pragma unroll
     for (int t = 0; t < NR; ++t)
       if (t1 + t < n_tiles) load_tile(t1 + t, v[t]);
   }

@@ -233,7 +233,7 @@ __device__ __forceinline__ void rot_lanes_tiles(const uint16_t *__restrict__ src
   static_assert(SL != 2 || (UNIT == 4 && OP == OP_QUANT && FMT != 2), "unit tiles: MX quantize, 4 per unit");
   static_assert(FMT == 2 || OP == OP_QUANT, "MX QDQ runs on k_rot_t16");
   const int64_t K = SL == 2 ? bl.groups * 32 : 0;
-  const int64_t col_pairs = SL == 2 ? bl.gblocks : 0;
+  const int64_t col_pairs = SL == 2 ? bl.gblocks : 1;  // (used only with SL 2)
   const int64_t n_tiles = SL == 2 ? 4 * ((bl.rows + 31) / 32) * col_pairs : (n_elem + TILE_ELEMS - 1) / TILE_ELEMS;
   const int64_t n_units = (n_tiles + UNIT - 1) / UNIT;
   // SL 2: first row and column of a tile, and whether its columns exist
