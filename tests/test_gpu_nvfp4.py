@@ -155,6 +155,26 @@ def test_rotated_within_band(mx, r, shape):
         nv_band_check(y, beta, g, deq_gpu=qdq.float().cpu().numpy().astype(np.float64))
 
 
+@pytest.mark.parametrize("r", [16, 32, 64, 128])
+def test_dense_nonsymmetric_rotation(mx, r):
+    """A dense matrix with no symmetry (seeded normal entries times r^-0.5,
+    rounded to bf16) on several tiles with a partial last one: quantize and
+    QDQ within the NVFP4 band of the oracle."""
+    import torch
+    rng = np.random.default_rng(950 + r)
+    Rb = W.f32_to_bf16_bits((rng.standard_normal((r, r)) / np.sqrt(r)).astype(np.float32))
+    x = W.random_bf16((300, 1152), seed=r + 11)
+    K = x.shape[1]
+    y, beta = oracle.rotate(x, Rb, r, threads=THREADS)
+    for g in (1.0, tensor_g(x) * 0.9):
+        xs, R = to_gpu_bf16(x), to_gpu_bf16(Rb)
+        codes, scales = mx.mx_nvfp4_quantize(xs, gscale(g), rot=R)
+        qdq = mx.mx_nvfp4_qdq(xs, gscale(g), rot=R)
+        torch.cuda.synchronize()
+        nv_band_check(y, beta, g, codes_gpu=unpack_codes(E2M1, bits_of(codes), K), scales_gpu=bits_of(scales))
+        nv_band_check(y, beta, g, deq_gpu=qdq.float().cpu().numpy().astype(np.float64))
+
+
 def test_rotated_full_size(mx):
     """Rotation 128 on the 8192 x 28672 layer: codes, scales and QDQ output
     of every row within the NVFP4 band of the oracle (tests/bandcheck.c), the

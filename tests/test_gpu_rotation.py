@@ -129,6 +129,24 @@ def test_hadamard_small_shapes(mx, fmt, r):
 
 
 @pytest.mark.parametrize("fmt", [E2M1, E4M3])
+@pytest.mark.parametrize("r", RS)
+def test_dense_nonsymmetric_rotation(mx, fmt, r):
+    """A dense matrix with no symmetry (seeded normal entries times r^-0.5,
+    rounded to bf16), so that R and its transpose rotate differently by far
+    more than the band: QDQ and quantize on every kernel of the rotation, on
+    shapes of several tiles with a partial last one, within the band."""
+    rng = np.random.default_rng(900 + r)
+    R = W.f32_to_bf16_bits((rng.standard_normal((r, r)) / np.sqrt(r)).astype(np.float32))
+    for shape in [(37, 1024), (300, 1152)]:
+        x = W.random_bf16(shape, seed=shape[0] + r + 7 * fmt)
+        y, beta = oracle.rotate(x, R, r, threads=THREADS)
+        yt, _ = oracle.rotate(x, np.ascontiguousarray(R.T), r, threads=THREADS)
+        assert (np.abs(yt - y) > beta).mean() > 0.5  # the transpose lies outside the band
+        _qdq_band(mx, fmt, x, R, r)
+        _quant_band(mx, fmt, x, R, r)
+
+
+@pytest.mark.parametrize("fmt", [E2M1, E4M3])
 @pytest.mark.parametrize("shape", [(255, 128), (256, 128), (257, 128), (511, 128), (512, 128), (513, 128),
                                    (31, 4224), (16, 8192), (3, 22016)],
                          ids=lambda s: f"{s[0]}x{s[1]}")
