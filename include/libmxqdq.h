@@ -226,6 +226,8 @@ MX_API int mx_matmul(int fmt, const uint8_t *a_codes, const uint8_t *a_scales,
  *   global_scale device pointer to one fp32, 4-byte aligned; read by the
  *                kernel (so it may be computed on the device).
  * Non-finite input, or g not positive and finite, is outside the contract.
+ * mx_nvfp4_qdq writes dst [M x K] bf16 (16-byte aligned); dst == src (an
+ * exact alias) is allowed there, as for mx_qdq.
  */
 MX_API int mx_nvfp4_quantize(const void *src, int64_t M, int64_t K,
                              const void *rot, int rot_size,

@@ -175,6 +175,22 @@ def test_dense_nonsymmetric_rotation(mx, r):
         nv_band_check(y, beta, g, deq_gpu=qdq.float().cpu().numpy().astype(np.float64))
 
 
+@pytest.mark.parametrize("r", [0, 16, 64, 128])
+def test_in_place_matches_out_of_place(mx, r):
+    """dst == src gives the bits of the out-of-place QDQ, on the unrotated,
+    the 32-block and the lane-owned kernels."""
+    import torch
+    x = W.random_bf16((2048, 4096), seed=31 + r)
+    g = tensor_g(x)
+    R = to_gpu_bf16(W.hadamard_rotation(r)) if r else None
+    src = to_gpu_bf16(x)
+    ref = mx.mx_nvfp4_qdq(src, gscale(g), rot=R)
+    t = src.clone()
+    mx.mx_nvfp4_qdq(t, gscale(g), rot=R, dst=t)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(t), bits_of(ref)), f"nvfp4 in place r={r}"
+
+
 def test_rotated_full_size(mx):
     """Rotation 128 on the 8192 x 28672 layer: codes, scales and QDQ output
     of every row within the NVFP4 band of the oracle (tests/bandcheck.c), the

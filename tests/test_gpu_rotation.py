@@ -146,6 +146,26 @@ def test_dense_nonsymmetric_rotation(mx, fmt, r):
         _quant_band(mx, fmt, x, R, r)
 
 
+@pytest.mark.parametrize("r", [0] + RS)
+def test_in_place_matches_out_of_place(mx, r):
+    """dst == src: every QDQ kernel reads each element before its own wave
+    writes it, so QDQ in place gives the bits it gives out of place (bf16 on
+    every rotation kernel, small and many-workgroup shapes; fp32 sources)."""
+    import torch
+    for shape in [(300, 1152), (4096, 8192)]:
+        x = W.random_bf16(shape, seed=77 + r + shape[0])
+        xf = W.random_f32(shape, seed=78 + r + shape[0])
+        R = to_gpu_bf16(W.hadamard_rotation(r)) if r else None
+        Rf = to_gpu_f32(W.hadamard_rotation(r, "f32")) if r else None
+        for fmt in (E2M1, E4M3):
+            for src, rot in ((to_gpu_bf16(x), R), (to_gpu_f32(xf), Rf)):
+                ref = mx.mx_qdq(fmt, src, rot=rot)
+                t = src.clone()
+                mx.mx_qdq(fmt, t, rot=rot, dst=t)
+                torch.cuda.synchronize()
+                assert np.array_equal(bits_of(t), bits_of(ref)), f"in place {shape} fmt{fmt} {src.dtype} r={r}"
+
+
 @pytest.mark.parametrize("fmt", [E2M1, E4M3])
 @pytest.mark.parametrize("shape", [(255, 128), (256, 128), (257, 128), (511, 128), (512, 128), (513, 128),
                                    (31, 4224), (16, 8192), (3, 22016)],
