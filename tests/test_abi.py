@@ -193,6 +193,27 @@ def test_status_strings_and_stream(lib):
     assert not lib.mx_get_stream()
 
 
+def test_stream_is_thread_local(lib):
+    """A stream set in one thread is not the stream of another."""
+    import threading
+    seen = {}
+
+    def worker(name, value):
+        lib.mx_set_stream(ctypes.c_void_p(value))
+        barrier.wait()
+        seen[name] = lib.mx_get_stream()
+        lib.mx_set_stream(None)
+
+    barrier = threading.Barrier(2)
+    ts = [threading.Thread(target=worker, args=("a", 0x1000)), threading.Thread(target=worker, args=("b", 0x2000))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert seen == {"a": 0x1000, "b": 0x2000}
+    assert not lib.mx_get_stream()
+
+
 def test_library_does_not_reference_the_oracle():
     """The product library links nothing from oracle/ (no orc_ symbols)."""
     import subprocess

@@ -251,6 +251,39 @@ def test_side_stream(mx):
     assert_bits_equal(bits_of(out), oracle.qdq(E2M1, x), "side stream")
 
 
+def test_two_threads_two_streams(mx):
+    """Two host threads, each on its own stream (the library's stream is
+    per thread), launch QDQ and quantize concurrently: each thread's results
+    equal those of the same calls made alone."""
+    import threading
+    import torch
+    xs = [to_gpu_bf16(W.random_bf16((1024, 8192), seed=40 + i)) for i in range(2)]
+    ref = []
+    for x in xs:
+        ref.append((mx.mx_qdq(E2M1, x), *mx.mx_quantize(E4M3, x)))
+    torch.cuda.synchronize()
+    got = [None, None]
+
+    def worker(i):
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            outs = []
+            for _ in range(8):
+                outs.append((mx.mx_qdq(E2M1, xs[i]), *mx.mx_quantize(E4M3, xs[i])))
+        s.synchronize()
+        got[i] = outs
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    for i in range(2):
+        for outs in got[i]:
+            for a, b in zip(outs, ref[i]):
+                assert torch.equal(a, b), f"thread {i}"
+
+
 def test_empty(mx):
     import torch
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
