@@ -31,6 +31,15 @@ MUTANTS = {
     "nvfp4_amax_first_only": ("if (fabsf(x[c + j]) > amax)", "if (j == 0)"),
     "exact_dequant_scale_bias": ("dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 127);",
                                  "dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 128);"),
+    "wrong_emax_e4m3": ("{4, 3, 7, -6, 8, 448.0}", "{4, 3, 7, -6, 7, 448.0}"),
+    "e4m3_max_480": ("{4, 3, 7, -6, 8, 448.0}", "{4, 3, 7, -6, 8, 480.0}"),
+    "bf16_rounded_one_bit_short": ("binary_bits(round_binary(x, 8, -126, 127), 8, 8, 127)",
+                                   "binary_bits(round_binary(x, 7, -126, 127), 8, 8, 127)"),
+    "f32_rounded_one_bit_short": ("binary_bits(round_binary(x, 24, -126, 127), 24, 8, 127)",
+                                  "binary_bits(round_binary(x, 23, -126, 127), 24, 8, 127)"),
+    "beta_without_abs": ("sabs += fabs(p);", "sabs += p;"),
+    "rotation_drops_last_term": ("for (int t = 0; t < r; ++t) {\n                double p",
+                                 "for (int t = 0; t < r - 1; ++t) {\n                double p"),
     "exact_dequant_sign_dropped": ("dst[idx] = (b == 0xFF) ? NAN : ldexp(orc_decode(fmt, code), b - 127);",
                                    "dst[idx] = (b == 0xFF) ? NAN : ldexp(fabs(orc_decode(fmt, code)), b - 127);"),
 }
