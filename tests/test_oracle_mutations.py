@@ -61,3 +61,35 @@ def test_pins_reject_planted_mistake(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
+
+
+# The GEMM reference's own step (the product of the two exact dequantized
+# operands) is Python: the same check on a planted copy of the package.
+PY_MUTANTS = {
+    "matmul_b_not_transposed": ("return a @ b.T", "return a @ b"),
+    "matmul_operands_swapped": ("return a @ b.T", "return b @ a.T"),
+}
+
+
+@pytest.mark.parametrize("name", ["unchanged"] + sorted(PY_MUTANTS))
+def test_pins_reject_planted_python_mistake(name, tmp_path):
+    """(The unchanged copy is the control: set up the same way, it passes.)"""
+    import oracle
+    old, new = PY_MUTANTS.get(name, ("return a @ b.T", "return a @ b.T"))
+    text = open(os.path.join(ROOT, "oracle", "__init__.py")).read()
+    assert text.count(old) == 1, name
+    (tmp_path / "oracle").mkdir()
+    (tmp_path / "oracle" / "__init__.py").write_text(text.replace(old, new))
+    env = dict(os.environ, MXORACLE_LIB=oracle.build(force=False),
+               PYTHONPATH=os.pathsep.join([str(tmp_path), ROOT]))
+    # run from the planted copy's folder, so that its package is the one imported
+    where = subprocess.run([sys.executable, "-c", "import oracle; print(oracle.__file__)"],
+                           cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=60)
+    assert where.stdout.strip().startswith(str(tmp_path)), where.stdout + where.stderr
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=600)
+    if name == "unchanged":
+        assert r.returncode == 0, r.stdout[-2000:]
+    else:
+        assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
