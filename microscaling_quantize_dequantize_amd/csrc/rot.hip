@@ -720,8 +720,7 @@ __device__ __forceinline__ void store_direct(const f32x16 &acc, int64_t blk, int
     if (valid) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        __builtin_nontemporal_store(f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]},
-                                    (f32x4 *)(d + 8 * q));
+        *(f32x4 *)(d + 8 * q) = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
     }
     return;
   }
@@ -739,7 +738,7 @@ __device__ __forceinline__ void store_direct(const f32x16 &acc, int64_t blk, int
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         v[e] = sb == 255u ? __uint_as_float(F32_NAN) : decode_code<FMT>((c[q] >> (CB * e)) & CM, s);
-      __builtin_nontemporal_store(v, (f32x4 *)(d + 8 * q));
+      *(f32x4 *)(d + 8 * q) = v;
     }
   }
 }
@@ -771,7 +770,7 @@ __global__ __launch_bounds__(DTHREADS) void k_rotate_bf16(const uint16_t *__rest
     const u32x4 *p = (const u32x4 *)(src + blk * RB) + h;
     u32x4 b[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) b[kb] = valid ? __builtin_nontemporal_load(p + 2 * kb) : u32x4{0u, 0u, 0u, 0u};
+    for (int kb = 0; kb < NKB; ++kb) b[kb] = valid ? p[2 * kb] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) {
       f32x16 acc = {};
@@ -805,7 +804,7 @@ __global__ __launch_bounds__(DTHREADS) void k_rot_f32(const float *__restrict__ 
     float xv[HALF];
 #pragma unroll
     for (int k4 = 0; k4 < HALF / 4; ++k4) {
-      const f32x4 v = valid ? __builtin_nontemporal_load(p + k4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 v = valid ? p[k4] : f32x4{0.f, 0.f, 0.f, 0.f};
       xv[4 * k4] = v[0];
       xv[4 * k4 + 1] = v[1];
       xv[4 * k4 + 2] = v[2];
