@@ -783,41 +783,81 @@ __global__ __launch_bounds__(DTHREADS) void k_rotate_bf16(const uint16_t *__rest
   }
 }
 
+// fp32 sources: the rotation on v_mfma_f32_32x32x2_f32, whose A and B
+// operands are one value per lane (layout above).  A workgroup's four waves
+// share steps of 16 KiB of input (TPS tiles of 32 blocks): wave w takes
+// output columns 32 (w % NCG) .. +31 of tile w / NCG, so it holds only those
+// columns of Reff, in registers (RB/2 values per lane), and one wave owns
+// each 32-group.  The input is loaded fully coalesced (1 KiB per
+// instruction) into one of two LDS step buffers, the next step's loads in
+// flight while the current one is rotated; lanes read their block's run
+// back 16 bytes at a time (four k-steps).  Pieces are XOR-swizzled so that
+// both the coalesced writes and the per-block reads are free of bank
+// conflicts.  Outputs go out from the MFMA layout (store_direct).
+template <int PPB>
+__device__ __forceinline__ int fslot(int b, int c) {
+  constexpr int BPR = PPB >= 16 ? 1 : 16 / PPB;  // blocks per 256-byte LDS row
+  constexpr int KM = PPB >= 16 ? 15 : PPB - 1;
+  return PPB * b + (c ^ ((b / BPR) & KM));
+}
+
 template <int FMT, int OP, int RB>
 __global__ __launch_bounds__(DTHREADS) void k_rot_f32(const float *__restrict__ src,
                                                       const float *__restrict__ rot, int r,
                                                       void *__restrict__ dst, int64_t n_blk) {
-  constexpr int NJT = RB / 32, HALF = RB / 2;
-  __shared__ float sA[NJT * HALF * 64];
-  for (int idx = threadIdx.x; idx < NJT * HALF * 64; idx += DTHREADS) {
-    const int ln = idx & 63, f = idx >> 6, jt = f / HALF, kb = f % HALF;
-    sA[idx] = reff(rot, r, (ln >> 5) * HALF + kb, jt * 32 + (ln & 31));
-  }
+  constexpr int NCG = RB / 32, TPS = (DTHREADS / 64) / NCG, HALF = RB / 2;
+  constexpr int PPB = RB / 4;                 // 16-byte pieces per block
+  constexpr int SP = TPS * 32 * PPB;          // pieces per step (1024: 16 KiB)
+  constexpr int NLD = SP / DTHREADS;          // pieces each thread loads per step
+  static_assert(NLD * DTHREADS == SP && TPS * NCG * 64 == DTHREADS, "whole steps");
+  __shared__ f32x4 buf[2][SP];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
+  const int cg = wave % NCG, tw = wave / NCG;
+  const int64_t n_steps = (n_blk + 32 * TPS - 1) / (32 * TPS);
+  const int64_t n_pieces = n_blk * PPB;
+  int64_t step = blockIdx.x;
+  if (step >= n_steps) return;  // (the whole workgroup)
+
+  auto load_step = [&](int64_t st, f32x4 *v) {
+    const f32x4 *g = (const f32x4 *)src + st * SP + threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < NLD; ++q)
+      v[q] = st * SP + q * DTHREADS + threadIdx.x < n_pieces ? __builtin_nontemporal_load(g + q * DTHREADS)
+                                                             : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto stage = [&](f32x4 *b, const f32x4 *v) {
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      const int P = q * DTHREADS + threadIdx.x;
+      b[fslot<PPB>(P / PPB, P % PPB)] = v[q];
+    }
+  };
+
+  f32x4 v[NLD];
+  load_step(step, v);
+  // this wave's columns of Reff: ra[kb] = Reff[h HALF + kb][32 cg + n]
+  float ra[HALF];
+#pragma unroll
+  for (int kb = 0; kb < HALF; ++kb) ra[kb] = reff(rot, r, h * HALF + kb, 32 * cg + n);
+  stage(buf[0], v);
   __syncthreads();
-  const int lane = threadIdx.x & 63, h = lane >> 5;
-  const int64_t n_tiles = (n_blk + 31) / 32;
-  for (int64_t tile = (int64_t)blockIdx.x * (DTHREADS / 64) + (threadIdx.x >> 6); tile < n_tiles;
-       tile += (int64_t)gridDim.x * (DTHREADS / 64)) {
-    const int64_t blk = tile * 32 + (lane & 31);
-    const bool valid = blk < n_blk;
-    const f32x4 *p = (const f32x4 *)(src + blk * RB + h * HALF);
-    float xv[HALF];
+  for (int cur = 0;; cur ^= 1) {
+    const int64_t next = step + gridDim.x;
+    if (next < n_steps) load_step(next, v);
+    const f32x4 *b = buf[cur];
+    f32x16 acc = {};
 #pragma unroll
     for (int k4 = 0; k4 < HALF / 4; ++k4) {
-      const f32x4 v = valid ? p[k4] : f32x4{0.f, 0.f, 0.f, 0.f};
-      xv[4 * k4] = v[0];
-      xv[4 * k4 + 1] = v[1];
-      xv[4 * k4 + 2] = v[2];
-      xv[4 * k4 + 3] = v[3];
-    }
+      const f32x4 x4 = b[fslot<PPB>(32 * tw + n, h * (HALF / 4) + k4)];
 #pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int kb = 0; kb < HALF; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sA[(jt * HALF + kb) * 64 + lane], xv[kb], acc, 0, 0, 0);
-      store_direct<FMT, OP, RB>(acc, blk, jt, h, valid, dst);
+      for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ra[4 * k4 + k], x4[k], acc, 0, 0, 0);
     }
+    const int64_t blk = step * 32 * TPS + 32 * tw + n;
+    store_direct<FMT, OP, RB>(acc, blk, cg, h, blk < n_blk, dst);
+    if (next >= n_steps) break;
+    stage(buf[cur ^ 1], v);  // buf[cur ^ 1] was last read before the previous barrier
+    __syncthreads();
+    step = next;
   }
 }
 
@@ -879,14 +919,20 @@ static void run_staged(const void *src, const void *rot, int r, void *dst, uint8
   }
 }
 
+template <int RB> constexpr int f32_per_cu() { return RB == 128 ? 8 : 3; }
+
 template <int FMT, int OP, int RB>
 static void run_direct(int dtype, const void *src, const void *rot, int r, void *dst, int64_t n, hipStream_t st) {
   const int64_t n_blk = n / RB;
-  const unsigned g = persistent_grid((n_blk + 31) / 32, DTHREADS / 64, 8);
-  if (dtype == 0)
+  if (dtype == 0) {
+    const unsigned g = persistent_grid((n_blk + 31) / 32, DTHREADS / 64, 8);
     k_rotate_bf16<RB><<<g, DTHREADS, 0, st>>>((const uint16_t *)src, (const uint16_t *)rot, r, (float *)dst, n_blk);
-  else
+  } else {
+    // one workgroup per 16 KiB step, persistent beyond f32_per_cu per CU
+    const int64_t tps = (DTHREADS / 64) / (RB / 32);
+    const unsigned g = persistent_grid((n_blk + 32 * tps - 1) / (32 * tps), 1, f32_per_cu<RB>());
     k_rot_f32<FMT, OP, RB><<<g, DTHREADS, 0, st>>>((const float *)src, (const float *)rot, r, dst, n_blk);
+  }
 }
 
 // Block size of the staged (bf16) kernels: RB = max(r, 32), except that
