@@ -3,6 +3,8 @@
 // call allocates, frees or synchronizes.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/libmxqdq.h"
 #include "launch.h"
 
@@ -41,15 +43,16 @@ int launched(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ELAUNCH; }
 namespace mx {
 
 int device_cu_count() {
-  static int cache[64] = {0};
+  // per device, filled on first use (threads that race here store the same value)
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 }  // namespace mx
