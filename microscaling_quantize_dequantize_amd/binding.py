@@ -76,6 +76,9 @@ def mx_set_stream(stream) -> None:
 def _dev(t: torch.Tensor, name: str) -> int:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        # the library launches on the current device (and torch's stream there)
+        raise ValueError(f"{name} is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
