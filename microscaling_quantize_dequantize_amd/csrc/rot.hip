@@ -711,6 +711,29 @@ void k_rot_t16(const uint16_t *__restrict__ src, const uint16_t *__restrict__ ro
 // v_mfma_f32_32x32x2_f32 takes one value per lane: lane l supplies
 // B[k = l/32][n = l%32] and A[m = l%32][k = l/32], and k-step kb covers
 // t = (l/32)*RB/2 + kb.
+// The fp32 outputs of one accumulator: o[q] = elements 8q + 4h .. +3 of the
+// block's 32 columns (the rotated values, or their QDQ by exact software
+// decode of the hardware codes).
+template <int FMT, int OP>
+__device__ __forceinline__ void direct_values(const f32x16 &acc, f32x4 (&o)[4]) {
+  if (OP == OP_ROTATE) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    return;
+  }
+  unsigned sb, c[4];
+  float sc;
+  group_codes<FMT>(acc, sb, sc, c);
+  const int s = (int)sb - 127;
+  constexpr int CB = FMT == 0 ? 4 : 8;
+  constexpr unsigned CM = (1u << CB) - 1u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[q][e] = sb == 255u ? __uint_as_float(F32_NAN) : decode_code<FMT>((c[q] >> (CB * e)) & CM, s);
+}
+
 template <int FMT, int OP, int RB>
 __device__ __forceinline__ void store_direct(const f32x16 &acc, int64_t blk, int jt, int h, bool valid,
                                              void *__restrict__ dst) {
@@ -811,6 +834,10 @@ __global__ __launch_bounds__(DTHREADS) void k_rot_f32(const float *__restrict__ 
   constexpr int NLD = SP / DTHREADS;          // pieces each thread loads per step
   static_assert(NLD * DTHREADS == SP && TPS * NCG * 64 == DTHREADS, "whole steps");
   __shared__ f32x4 buf[2][SP];
+  // RB <= 64: each wave's outputs go out through LDS in whole 128-byte
+  // column runs (3% faster there; at RB = 128 the extra registers cost more)
+  constexpr bool OSTAGE = RB <= 64;
+  __shared__ f32x4 obuf[OSTAGE ? DTHREADS / 64 : 1][OSTAGE ? 256 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
   const int cg = wave % NCG, tw = wave / NCG;
   const int64_t n_steps = (n_blk + 32 * TPS - 1) / (32 * TPS);
@@ -852,8 +879,27 @@ __global__ __launch_bounds__(DTHREADS) void k_rot_f32(const float *__restrict__ 
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ra[4 * k4 + k], x4[k], acc, 0, 0, 0);
     }
-    const int64_t blk = step * 32 * TPS + 32 * tw + n;
-    store_direct<FMT, OP, RB>(acc, blk, cg, h, blk < n_blk, dst);
+    if constexpr (OSTAGE) {
+      // piece 2q + h of block n in the wave's buffer (keyed like tslot),
+      // then 8 blocks' column runs per store instruction
+      f32x4 o[4];
+      direct_values<FMT, OP>(acc, o);
+      f32x4 *ob = obuf[wave];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ob[8 * n + ((2 * q + h) ^ ((n >> 1) & 7))] = o[q];
+      wave_lds_sync();
+      const int64_t blk0 = step * 32 * TPS + 32 * tw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int P = 64 * i + lane, bn = P >> 3, c = P & 7;
+        const f32x4 w = ob[8 * bn + (c ^ ((bn >> 1) & 7))];
+        if (blk0 + bn < n_blk) *((f32x4 *)((float *)dst + (blk0 + bn) * RB + 32 * cg) + c) = w;
+      }
+      wave_lds_sync();
+    } else {
+      const int64_t blk = step * 32 * TPS + 32 * tw + n;
+      store_direct<FMT, OP, RB>(acc, blk, cg, h, blk < n_blk, dst);
+    }
     if (next >= n_steps) break;
     stage(buf[cur ^ 1], v);  // buf[cur ^ 1] was last read before the previous barrier
     __syncthreads();
