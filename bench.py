@@ -34,7 +34,8 @@ Beside the step:
     28672 x 8192 layers; inputs under 1 GB are evicted from the 256 MB
     last-level cache between timed launches by a 512 MiB write;
   - dequantize, the layer read as 57344 x 8192, fp32 sources (QDQ without
-    rotation, and with rotation 128 on the fp32 matrix cores), NVFP4,
+    rotation, with rotation 16, and with rotation 128 on the fp32 matrix
+    cores), NVFP4,
     blocked scales and the GEMM that consumes the quantized layer.
 The CPU baseline runs the oracle (unchanged) on a bounded row sample of the
 same layer and variants, on the host's cores.
@@ -447,20 +448,21 @@ def main():
                        "frac_of_peak": round(4 * n / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)})
     del deq_out
     # fp32 sources (fp32 in, fp32 out: 8 bytes per element): QDQ without
-    # rotation, and with rotation 128, whose contraction runs on the fp32
-    # matrix cores (256 flops per element against their 157.3 TFLOP/s)
+    # rotation, with rotation 16, and with rotation 128, whose contraction is
+    # bound by the fp32 matrix cores (256 flops per element against their
+    # 157.3 TFLOP/s)
     xf = x.float()
     df = torch.empty_like(xf)
-    Rf = torch.from_numpy(W.hadamard_rotation(128, "f32")).to(dev)
-    for fmt, r in ((0, 0), (1, 0), (0, 128)):
-        R = Rf if r else None
+    Rf = {r: torch.from_numpy(W.hadamard_rotation(r, "f32")).to(dev) for r in (16, 128)}
+    for fmt, r in ((0, 0), (1, 0), (0, 16), (0, 128)):
+        R = Rf[r] if r else None
         mx.mx_qdq(fmt, xf, rot=R, dst=df)
         avg, mn = timed(lambda: mx.mx_qdq(fmt, xf, rot=R, dst=df), 10)
         e = {"kernel": f"qdq_{'mxfp4' if fmt == 0 else 'mxfp8'}_f32_rot{r}", "bytes": 8 * n,
              "avg_us": round(avg * 1e3, 2), "min_us": round(mn * 1e3, 2),
              "GBps": round(8 * n / (avg * 1e-3) / 1e9, 1),
              "frac_of_peak": round(8 * n / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)}
-        if r:
+        if r == 128:
             e.update({"flops": 2 * r * n, "TFLOPs": round(2 * r * n / (avg * 1e-3) / 1e12, 1),
                       "peak_TFLOPs": 157.3,
                       "frac_of_mfma_peak": round(2 * r * n / (avg * 1e-3) / 1e12 / 157.3, 4)})
