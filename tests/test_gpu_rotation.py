@@ -300,6 +300,21 @@ def test_fp32_source_rotated(mx, fmt, r):
     assert_bits_equal(bits_of(out), oracle.qdq(fmt, x, Pm, r), "f32 permutation")
 
 
+@pytest.mark.parametrize("fmt,r", [(E2M1, 16), (E4M3, 64), (E2M1, 128), (E4M3, 128)])
+def test_fp32_source_rotated_many_steps(mx, fmt, r):
+    """fp32 sources on a tensor of more 16 KiB steps than the grid has
+    workgroups (so workgroups loop) and a partial last step: QDQ within the
+    band of the oracle on every element."""
+    import torch
+    M, K = 8200, 1152
+    x = W.random_f32((M, K), seed=700 + r)
+    R = (W.sylvester_hadamard(r) / np.sqrt(r)).astype(np.float32)
+    out = mx.mx_qdq(fmt, to_gpu_f32(x), rot=to_gpu_f32(R))
+    torch.cuda.synchronize()
+    y, beta = oracle.rotate(x, R, r, threads=THREADS)
+    band_check(fmt, y, beta, deq_gpu=bits_of(out).view(np.float32).astype(np.float64), dst_bf16=False)
+
+
 def _spread_mask(nonfinite, block):
     """Groups [M, K/32] and elements [M, K] of every `block`-element block of a
     row that holds a non-finite input."""
