@@ -304,15 +304,18 @@ def test_fp32_source_rotated(mx, fmt, r):
 def test_fp32_source_rotated_many_steps(mx, fmt, r):
     """fp32 sources on a tensor of more 16 KiB steps than the grid has
     workgroups (so workgroups loop) and a partial last step: QDQ within the
-    band of the oracle on every element."""
+    band of the oracle on every element, and the rotation alone within
+    beta."""
     import torch
     M, K = 8200, 1152
     x = W.random_f32((M, K), seed=700 + r)
     R = (W.sylvester_hadamard(r) / np.sqrt(r)).astype(np.float32)
     out = mx.mx_qdq(fmt, to_gpu_f32(x), rot=to_gpu_f32(R))
+    yg = mx.mx_rotate(to_gpu_f32(x), to_gpu_f32(R))
     torch.cuda.synchronize()
     y, beta = oracle.rotate(x, R, r, threads=THREADS)
     band_check(fmt, y, beta, deq_gpu=bits_of(out).view(np.float32).astype(np.float64), dst_bf16=False)
+    rotate_within_beta(bits_of(yg).view(np.float32), y, beta)
 
 
 def _spread_mask(nonfinite, block):
