@@ -4,8 +4,8 @@ Every function has the name of the C entry point it calls and takes torch
 tensors on the GPU.  Before anything is enqueued it checks every tensor it
 is handed: dtype and exact shape first (codes [M, K/2] or [M, K], scales
 [M, K/32] or [M, K/16] for NVFP4, blocked scales at least the blocked size,
-outputs [M, K] in the stated dtype), then that each is a contiguous device
-tensor; a mismatch raises ValueError or TypeError.  It then points the
+outputs [M, K] in the stated dtype), then that each is a contiguous tensor
+on the current device; a mismatch raises ValueError or TypeError.  It then points the
 library at torch's current stream and passes raw pointers.  All computation
 happens in the HIP kernels; there is no fallback: if the library is missing
 the import fails.
