@@ -768,44 +768,6 @@ __device__ __forceinline__ void store_direct(const f32x16 &acc, int64_t blk, int
 
 constexpr int DTHREADS = 256;
 
-template <int RB>
-__global__ __launch_bounds__(DTHREADS) void k_rotate_bf16(const uint16_t *__restrict__ src,
-                                                          const uint16_t *__restrict__ rot, int r,
-                                                          float *__restrict__ dst, int64_t n_blk) {
-  constexpr int NJT = RB / 32, NKB = RB / 16;
-  __shared__ u32x4 sA[NJT * NKB * 64];
-  for (int idx = threadIdx.x; idx < NJT * NKB * 64; idx += DTHREADS) {
-    const int ln = idx & 63, f = idx >> 6, jt = f / NKB, kb = f % NKB;
-    const int j = jt * 32 + (ln & 31), t0 = 16 * kb + 8 * (ln >> 5);
-    unsigned w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = (unsigned)reff(rot, r, t0 + 2 * i, j) | ((unsigned)reff(rot, r, t0 + 2 * i + 1, j) << 16);
-    sA[idx] = u32x4{w[0], w[1], w[2], w[3]};
-  }
-  __syncthreads();
-  const int lane = threadIdx.x & 63, h = lane >> 5;
-  const int64_t n_tiles = (n_blk + 31) / 32;
-  for (int64_t tile = (int64_t)blockIdx.x * (DTHREADS / 64) + (threadIdx.x >> 6); tile < n_tiles;
-       tile += (int64_t)gridDim.x * (DTHREADS / 64)) {
-    const int64_t blk = tile * 32 + (lane & 31);
-    const bool valid = blk < n_blk;
-    const u32x4 *p = (const u32x4 *)(src + blk * RB) + h;
-    u32x4 b[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) b[kb] = valid ? p[2 * kb] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sA[(jt * NKB + kb) * 64 + lane]),
-                                                      __builtin_bit_cast(bf16x8, b[kb]), acc, 0, 0, 0);
-      store_direct<0, OP_ROTATE, RB>(acc, blk, jt, h, valid, dst);
-    }
-  }
-}
-
 // fp32 sources: the rotation on v_mfma_f32_32x32x2_f32, whose A and B
 // operands are one value per lane (layout above).  A workgroup's four waves
 // share steps of 16 KiB of input (TPS tiles of 32 blocks): wave w takes
@@ -908,6 +870,95 @@ __global__ __launch_bounds__(DTHREADS) void k_rot_f32(const float *__restrict__ 
 }
 
 
+// The rotation alone of bf16 sources (fp32 out), on the same plan as the
+// fp32-source kernel above: a workgroup's four waves share steps of 8 KiB
+// of input (TPS tiles of 32 blocks), loaded coalesced into one of two
+// swizzled LDS buffers with the next step's loads in flight; wave w keeps
+// the MFMA fragments of its 32 output columns of Reff in registers and reads
+// its block's 16 bytes per k-step back (32x32x16 layout: k-step kb covers
+// t = 16 kb + 8 (l/32) + i).
+template <int RB>
+__global__ __launch_bounds__(DTHREADS) void k_rotate_bf16(const uint16_t *__restrict__ src,
+                                                          const uint16_t *__restrict__ rot, int r,
+                                                          float *__restrict__ dst, int64_t n_blk) {
+  constexpr int NCG = RB / 32, TPS = (DTHREADS / 64) / NCG, NKB = RB / 16;
+  constexpr int PPB = RB / 8;                 // 16-byte pieces per block
+  constexpr int SP = TPS * 32 * PPB;          // pieces per step (512: 8 KiB)
+  constexpr int NLD = SP / DTHREADS;
+  static_assert(NLD * DTHREADS == SP && TPS * NCG * 64 == DTHREADS, "whole steps");
+  __shared__ u32x4 buf[2][SP];
+  __shared__ f32x4 obuf[DTHREADS / 64][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
+  const int cg = wave % NCG, tw = wave / NCG;
+  const int64_t n_steps = (n_blk + 32 * TPS - 1) / (32 * TPS);
+  const int64_t n_pieces = n_blk * PPB;
+  int64_t step = blockIdx.x;
+  if (step >= n_steps) return;  // (the whole workgroup)
+
+  auto load_step = [&](int64_t st, u32x4 *v) {
+    const u32x4 *g = (const u32x4 *)src + st * SP + threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < NLD; ++q)
+      v[q] = st * SP + q * DTHREADS + threadIdx.x < n_pieces ? __builtin_nontemporal_load(g + q * DTHREADS)
+                                                             : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto stage = [&](u32x4 *b, const u32x4 *v) {
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      const int P = q * DTHREADS + threadIdx.x;
+      b[fslot<PPB>(P / PPB, P % PPB)] = v[q];
+    }
+  };
+
+  u32x4 v[NLD];
+  load_step(step, v);
+  // A fragments of this wave's columns: Reff[16 kb + 8h + i][32 cg + n]
+  u32x4 ra[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const int t0 = 16 * kb + 8 * h, j = 32 * cg + n;
+    unsigned w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (unsigned)reff(rot, r, t0 + 2 * i, j) | ((unsigned)reff(rot, r, t0 + 2 * i + 1, j) << 16);
+    ra[kb] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+  stage(buf[0], v);
+  __syncthreads();
+  for (int cur = 0;; cur ^= 1) {
+    const int64_t next = step + gridDim.x;
+    if (next < n_steps) load_step(next, v);
+    const u32x4 *b = buf[cur];
+    f32x16 acc = {};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ra[kb]),
+                                                    __builtin_bit_cast(bf16x8, b[fslot<PPB>(32 * tw + n, 2 * kb + h)]),
+                                                    acc, 0, 0, 0);
+    {
+      // outputs through the wave's LDS buffer, then 8 blocks' whole 128-byte
+      // column runs per store instruction
+      f32x4 *ob = obuf[wave];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        ob[8 * n + ((2 * q + h) ^ ((n >> 1) & 7))] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+      wave_lds_sync();
+      const int64_t blk0 = step * 32 * TPS + 32 * tw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int P = 64 * i + lane, bn = P >> 3, c = P & 7;
+        const f32x4 w = ob[8 * bn + (c ^ ((bn >> 1) & 7))];
+        if (blk0 + bn < n_blk) *((f32x4 *)(dst + (blk0 + bn) * RB + 32 * cg) + c) = w;
+      }
+      wave_lds_sync();
+    }
+    if (next >= n_steps) break;
+    stage(buf[cur ^ 1], v);  // buf[cur ^ 1] was last read before the previous barrier
+    __syncthreads();
+    step = next;
+  }
+}
+
 static unsigned persistent_grid(int64_t tiles, int waves, int per_cu) {
   int64_t g = (tiles + waves - 1) / waves;
   const int64_t cap = (int64_t)device_cu_count() * per_cu;
@@ -971,7 +1022,8 @@ template <int FMT, int OP, int RB>
 static void run_direct(int dtype, const void *src, const void *rot, int r, void *dst, int64_t n, hipStream_t st) {
   const int64_t n_blk = n / RB;
   if (dtype == 0) {
-    const unsigned g = persistent_grid((n_blk + 31) / 32, DTHREADS / 64, 8);
+    const int64_t tps = (DTHREADS / 64) / (RB / 32);
+    const unsigned g = persistent_grid((n_blk + 32 * tps - 1) / (32 * tps), 1, RB == 128 ? 4 : f32_per_cu<RB>());
     k_rotate_bf16<RB><<<g, DTHREADS, 0, st>>>((const uint16_t *)src, (const uint16_t *)rot, r, (float *)dst, n_blk);
   } else {
     // one workgroup per 16 KiB step, persistent beyond f32_per_cu per CU

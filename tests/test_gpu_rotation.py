@@ -318,6 +318,20 @@ def test_fp32_source_rotated_many_steps(mx, fmt, r):
     rotate_within_beta(bits_of(yg).view(np.float32), y, beta)
 
 
+@pytest.mark.parametrize("r", [16, 64, 128])
+def test_rotate_bf16_many_steps(mx, r):
+    """The rotation alone of bf16 sources on a tensor of more steps than the
+    grid has workgroups and a partial last step, within beta everywhere."""
+    import torch
+    M, K = 8200, 1152
+    x = W.random_bf16((M, K), seed=800 + r)
+    R = W.hadamard_rotation(r)
+    yg = mx.mx_rotate(to_gpu_bf16(x), to_gpu_bf16(R))
+    torch.cuda.synchronize()
+    y, beta = oracle.rotate(x, R, r, threads=THREADS)
+    rotate_within_beta(bits_of(yg).view(np.float32), y, beta)
+
+
 def _spread_mask(nonfinite, block):
     """Groups [M, K/32] and elements [M, K] of every `block`-element block of a
     row that holds a non-finite input."""
