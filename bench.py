@@ -35,7 +35,7 @@ Beside the step:
     last-level cache between timed launches by a 512 MiB write;
   - dequantize, the layer read as 57344 x 8192, fp32 sources (QDQ without
     rotation, with rotation 16, and with rotation 128 on the fp32 matrix
-    cores), NVFP4,
+    cores), the rotation alone (r = 16, 128), NVFP4,
     blocked scales and the GEMM that consumes the quantized layer.
 The CPU baseline runs the oracle (unchanged) on a bounded row sample of the
 same layer and variants, on the host's cores.
@@ -468,6 +468,15 @@ def main():
                       "frac_of_mfma_peak": round(2 * r * n / (avg * 1e-3) / 1e12 / 157.3, 4)})
         extras.append(e)
     del xf, df
+    # the rotation alone (bf16 in, fp32 out: 2 + 4 bytes per element)
+    yf = torch.empty((M, K), dtype=torch.float32, device=dev)
+    for r in (16, 128):
+        mx.mx_rotate(x, rots[r][1], dst=yf)
+        avg, mn = timed(lambda: mx.mx_rotate(x, rots[r][1], dst=yf), 10)
+        extras.append({"kernel": f"rotate_bf16_rot{r}", "bytes": 6 * n, "avg_us": round(avg * 1e3, 2),
+                       "min_us": round(mn * 1e3, 2), "GBps": round(6 * n / (avg * 1e-3) / 1e9, 1),
+                       "frac_of_peak": round(6 * n / (avg * 1e-3) / 1e9 / PEAK_GBPS, 4)})
+    del yf
     # NVFP4 (16-groups, E4M3 scales, per-tensor multiplier 448*6/amax) on the
     # same layer: QDQ and quantize, without rotation and with rotation 128
     gsc = (448.0 * 6.0 / x.abs().max().float()).reshape(1).contiguous()
