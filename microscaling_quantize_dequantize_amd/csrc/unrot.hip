@@ -237,9 +237,12 @@ static unsigned grid_for(int64_t n_pieces, int64_t per_block) {
 // out per lane) measured 2% faster with 64-thread blocks than with 128 or
 // 256 (MXFP4 QDQ on the 8192 x 57344 layer 288 -> 281 us, MXFP8 285 -> 282
 // us, same-process A/B), while quantize and dequantize, whose streams are
-// mostly reads or mostly writes, measured 1-10% slower with them.
+// mostly reads or mostly writes, measured 1-10% slower with them.  fp32
+// QDQ, also copy-shaped, likewise: 1% faster than 128 threads (MXFP4 577 ->
+// 571 us, MXFP8 568 -> 562 us on the layer in fp32), and 128 threads with
+// two pieces, 256 threads, or 64 with two pieces were slower.
 constexpr int QDQ_T = 64, QDQ_U = 1;
-constexpr int F32_T = 128, F32_U = 1;
+constexpr int F32_T = 64, F32_U = 1;
 constexpr int QNT_T = 128, QNT_U = 2;
 constexpr int DEQ_T = 128;
 template <int DT> constexpr int deq_unroll() { return DT == 0 ? 2 : 1; }
